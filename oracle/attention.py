@@ -1,0 +1,200 @@
+"""Naive float64 causal attention over the block-paged KV cache.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+What is computed ("1Cat-vLLM 1.5.0" RELEASE notes, "Flash-V100 long-context
+improvements": paged prefill, decode and the grouped q8 verifier are all the
+same attention over the paged prefix; "SM70 release profile": prompts are
+prefilled in chunks that attend to the pages already written):
+
+For sequence b with ``ctx_b`` keys (every key visible to its last query,
+including the new tokens) and ``q_len_b`` new queries, query i sits at
+position ``pos = ctx_b - q_len_b + i`` and attends keys ``0..pos``. For query
+head h the KV head is ``g = h // G`` with ``G = Hq / Hkv`` (contiguous head
+groups). With K, V the dequantized keys and values of head g:
+
+    s_j = softmax_scale * (q . K_j)            for j <= pos
+    m   = max_j s_j,   p_j = exp(s_j - m),   l = sum_j p_j
+    o   = sum_j p_j V_j / l
+
+A row with no visible key (pos < 0, e.g. ``ctx_b == 0``) has o = 0,
+m = -inf, l = 0.
+
+``softmax_scale`` is a float32 and is widened to float64. Decode is
+``q_len = 1``, verify ``q_len = 8`` (any q_len works), prefill one chunk of
+``q_len`` tokens. Splitting keys into partitions is not part of the
+definition; ``attend_partitioned`` exists only to self-test the log-sum-exp
+combine algebra.
+
+Rows are processed a block at a time purely to bound memory; each row's
+arithmetic is the definition above.
+"""
+
+import numpy as np
+
+from . import paged
+
+
+def _rows_attend(qrows, pos, K, V, scale):
+    """qrows [R, D] float64, pos [R] int. Returns o [R, D], m [R], l [R], P [R, ctx]."""
+    R, D = qrows.shape
+    ctx = K.shape[0]
+    o = np.zeros((R, D))
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    P = np.zeros((R, ctx))
+    if ctx == 0:
+        return o, m, l, P
+    s = scale * (qrows @ K.T)                       # [R, ctx]
+    j = np.arange(ctx)
+    visible = j[None, :] <= pos[:, None]
+    has = visible.any(axis=1)
+    s = np.where(visible, s, -np.inf)
+    m_h = s[has].max(axis=1)
+    p = np.exp(s[has] - m_h[:, None])              # masked keys -> exp(-inf) = 0
+    l_h = p.sum(axis=1)
+    o[has] = (p @ V) / l_h[:, None]
+    m[has] = m_h
+    l[has] = l_h
+    P[has] = p / l_h[:, None]
+    return o, m, l, P
+
+
+def attend(q, q_lens, ctx_lens, k_cache, v_cache, block_tables, fmt,
+           num_kv_heads, softmax_scale, k_scale=None, v_scale=None,
+           return_probs=False, row_block=256):
+    """q: [total_q, Hq, D] (sequences concatenated, seq b owns q_lens[b] rows).
+    Returns o [total_q, Hq, D] float64, m and l [total_q, Hq]
+    (m in natural-log units), and the probabilities when asked (tiny inputs)."""
+    q = np.asarray(q)
+    total_q, Hq, D = q.shape
+    Hkv = int(num_kv_heads)
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    scale = np.float64(np.float32(softmax_scale))
+    o = np.zeros((total_q, Hq, D))
+    m = np.full((total_q, Hq), -np.inf)
+    l = np.zeros((total_q, Hq))
+    probs = {} if return_probs else None
+    start = 0
+    for b, (qlen, ctx) in enumerate(zip(q_lens, ctx_lens)):
+        qlen, ctx = int(qlen), int(ctx)
+        for g in range(Hkv):
+            K, V = paged.gather(k_cache, v_cache, block_tables[b], ctx, g, fmt,
+                                k_scale, v_scale)
+            for i0 in range(0, qlen, row_block):
+                i1 = min(qlen, i0 + row_block)
+                for gh in range(G):
+                    h = g * G + gh
+                    rows = q[start + i0:start + i1, h, :].astype(np.float64)
+                    pos = ctx - qlen + np.arange(i0, i1)
+                    ob, mb, lb, Pb = _rows_attend(rows, pos, K, V, scale)
+                    o[start + i0:start + i1, h] = ob
+                    m[start + i0:start + i1, h] = mb
+                    l[start + i0:start + i1, h] = lb
+                    if return_probs:
+                        for r in range(i1 - i0):
+                            probs[(start + i0 + r, h)] = Pb[r]
+        start += qlen
+    if return_probs:
+        return o, m, l, probs
+    return o, m, l
+
+
+def attend_rows(q_rows, heads, positions, seq_ctx, k_cache, v_cache, block_table,
+                fmt, num_q_heads, num_kv_heads, softmax_scale, k_scale=None, v_scale=None):
+    """The same definition for a handful of sampled rows of one sequence:
+    q_rows [R, D], heads [R], positions [R]. Used where the full output is
+    too large for the oracle (rows are independent)."""
+    G = num_q_heads // num_kv_heads
+    scale = np.float64(np.float32(softmax_scale))
+    out = np.zeros((len(heads), q_rows.shape[1]))
+    cache = {}
+    for r, (h, pos) in enumerate(zip(heads, positions)):
+        g = int(h) // G
+        if g not in cache:
+            cache[g] = paged.gather(k_cache, v_cache, block_table, seq_ctx, g, fmt,
+                                    k_scale, v_scale)
+        K, V = cache[g]
+        ob, _, _, _ = _rows_attend(np.asarray(q_rows[r:r + 1], dtype=np.float64),
+                                   np.array([pos]), K, V, scale)
+        out[r] = ob[0]
+    return out
+
+
+def decode(q, ctx_lens, k_cache, v_cache, block_tables, fmt, num_kv_heads,
+           softmax_scale, k_scale=None, v_scale=None):
+    """q [B, Hq, D]: one query per sequence at position ctx_b - 1."""
+    B = q.shape[0]
+    o, m, l = attend(q, [1] * B, ctx_lens, k_cache, v_cache, block_tables, fmt,
+                     num_kv_heads, softmax_scale, k_scale, v_scale)
+    return o
+
+
+def verify(q, ctx_lens, k_cache, v_cache, block_tables, fmt, num_kv_heads,
+           softmax_scale, k_scale=None, v_scale=None):
+    """q [B, q_len, Hq, D]: the q_len newest positions of each sequence, each
+    attending causally (the grouped speculative-verify step)."""
+    B, qlen, Hq, D = q.shape
+    o, m, l = attend(q.reshape(B * qlen, Hq, D), [qlen] * B, ctx_lens, k_cache,
+                     v_cache, block_tables, fmt, num_kv_heads, softmax_scale,
+                     k_scale, v_scale)
+    return o.reshape(B, qlen, Hq, D)
+
+
+def attend_partitioned(q, q_lens, ctx_lens, k_cache, v_cache, block_tables, fmt,
+                       num_kv_heads, softmax_scale, partition_len,
+                       k_scale=None, v_scale=None):
+    """Split-KV form: keys [p*L, (p+1)*L) form partition p. Each partition
+    yields (m_p, l_p, O_p = sum_j exp(s_j - m_p) V_j); partitions are merged by
+    M = max_p m_p, w_p = exp(m_p - M), o = sum_p w_p O_p / sum_p w_p l_p.
+    Partitions with no visible key (m_p = -inf, l_p = 0) are left out."""
+    q = np.asarray(q)
+    total_q, Hq, D = q.shape
+    Hkv = int(num_kv_heads)
+    G = Hq // Hkv
+    scale = np.float64(np.float32(softmax_scale))
+    L = int(partition_len)
+    o = np.zeros((total_q, Hq, D))
+    start = 0
+    for b, (qlen, ctx) in enumerate(zip(q_lens, ctx_lens)):
+        qlen, ctx = int(qlen), int(ctx)
+        for g in range(Hkv):
+            K, V = paged.gather(k_cache, v_cache, block_tables[b], ctx, g, fmt,
+                                k_scale, v_scale)
+            for i in range(qlen):
+                pos = ctx - qlen + i
+                for gh in range(G):
+                    h = g * G + gh
+                    qv = q[start + i, h].astype(np.float64)
+                    parts = []
+                    for p0 in range(0, max(ctx, 1), L):
+                        hi = min(p0 + L, pos + 1)
+                        if hi <= p0:
+                            continue
+                        s = scale * (K[p0:hi] @ qv)
+                        mp = s.max()
+                        e = np.exp(s - mp)
+                        parts.append((mp, e.sum(), e @ V[p0:hi]))
+                    if not parts:
+                        continue
+                    M = max(mp for mp, _, _ in parts)
+                    w = [np.exp(mp - M) for mp, _, _ in parts]
+                    num = sum(wp * Op for wp, (_, _, Op) in zip(w, parts))
+                    den = sum(wp * lp for wp, (_, lp, _) in zip(w, parts))
+                    o[start + i, h] = num / den
+        start += qlen
+    return o
+
+
+def useful_flops(q_lens, ctx_lens, num_q_heads, head_dim):
+    """"Useful causal" FLOPs (counting only unmasked work, as the 1.5.0 notes
+    do for the long-prefill kernel): 4 * D per visible (query head, key) pair,
+    2 * D for q.k and 2 * D for p * v."""
+    pairs = 0
+    for qlen, ctx in zip(q_lens, ctx_lens):
+        qlen, ctx = int(qlen), int(ctx)
+        for i in range(qlen):
+            pairs += max(0, ctx - qlen + i + 1)
+    return 4 * head_dim * num_q_heads * pairs

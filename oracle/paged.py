@@ -1,0 +1,87 @@
+"""Block-paged KV cache: layout, quantize-on-write and gather, in plain numpy.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+Paging follows "SM70 release profile and acceleration status" (KV stored in
+fixed-size token pages, 2048 tokens in the release profile, 16 as the
+``--block-size 16`` alternative) and "1Cat-vLLM 1.5.0", section "Cache, memory
+and mixed-batch reliability" (block tables hold physical page ids). The pages
+do not fix a byte layout; the library's documented layout is restated here:
+
+* key cache   ``[num_blocks, num_kv_heads, block_size, head_dim]``
+  (token-major inside one page of one head),
+* value cache ``[num_blocks, num_kv_heads, head_dim, block_size]``
+  (dimension-major inside one page of one head).
+
+Token j of a sequence lives in physical page ``block_table[j // block_size]``
+at offset ``j % block_size``. A write goes to ``slot = page * block_size +
+offset``; a negative slot means "skip this token".
+
+Cache element formats: ``"f16"`` (numpy float16 values), ``"e4m3"`` and
+``"e5m2"`` (uint8 codes, see ``oracle.fp8``).
+"""
+
+import numpy as np
+
+from . import fp8
+
+F16 = "f16"
+E4M3 = fp8.E4M3
+E5M2 = fp8.E5M2
+
+
+def new_caches(num_blocks, num_kv_heads, block_size, head_dim, fmt, fill=0):
+    dt = np.float16 if fmt == F16 else np.uint8
+    kc = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=dt)
+    vc = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=dt)
+    return kc, vc
+
+
+def quantize(x, fmt, scale=None):
+    """Cache representation of values x: fp16 copy or FP8 codes."""
+    if fmt == F16:
+        return np.asarray(x).astype(np.float16)
+    return fp8.encode(x, fmt, scale)
+
+
+def write(k, v, slot_mapping, k_cache, v_cache, fmt, k_scale=None, v_scale=None):
+    """Quantize-on-write. k, v: [T, Hkv, D]; k_scale, v_scale: [Hkv] float32
+    (per KV head) or None. Writes in place, one token at a time."""
+    T, Hkv, D = k.shape
+    bs = k_cache.shape[2]
+    for t in range(T):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        page, off = slot // bs, slot % bs
+        for h in range(Hkv):
+            ks = None if k_scale is None else k_scale[h]
+            vs = None if v_scale is None else v_scale[h]
+            k_cache[page, h, off, :] = quantize(k[t, h, :], fmt, ks)
+            v_cache[page, h, :, off] = quantize(v[t, h, :], fmt, vs)
+
+
+def dequant(codes, fmt, scale=None):
+    """float64 values of cache elements."""
+    if fmt == F16:
+        return np.asarray(codes, dtype=np.float16).astype(np.float64)
+    return fp8.dequant(codes, fmt, scale)
+
+
+def gather(k_cache, v_cache, block_table, ctx, g, fmt, k_scale=None, v_scale=None):
+    """Dequantized K and V ([ctx, D] float64 each) of KV head g for one
+    sequence. Only the first ceil(ctx / block_size) block-table entries are
+    read, so padding entries are never dereferenced."""
+    bs = k_cache.shape[2]
+    D = k_cache.shape[3]
+    if ctx == 0:
+        return np.zeros((0, D)), np.zeros((0, D))
+    j = np.arange(ctx)
+    used = -(-ctx // bs)
+    pages = np.asarray(block_table[:used], dtype=np.int64)[j // bs]
+    off = j % bs
+    k_raw = k_cache[pages, g, off, :]              # [ctx, D]
+    v_raw = v_cache[pages, g, :, off]              # [ctx, D]
+    ks = None if k_scale is None else k_scale[g]
+    vs = None if v_scale is None else v_scale[g]
+    return dequant(k_raw, fmt, ks), dequant(v_raw, fmt, vs)
