@@ -1,0 +1,399 @@
+// Split-KV paged decode and grouped speculative verify, plus the log-sum-exp
+// combine.
+//
+// What the pages describe ("1Cat-vLLM 1.5.0" RELEASE notes, "Flash-V100
+// long-context improvements"): batched FP8 decode that loads each page id once
+// and reuses it for the page's K and V loads, with cache loads widened to 128
+// bits; long-context E4M3 decode routing at 128K/256K; and a grouped q8
+// verifier that treats the seven drafts plus one of a sequence as one group
+// over a single pass of the KV stream. How it is done here (gfx950):
+//
+// * Work-group (partition p, KV head g, sequence b), 4 waves. The partition's
+//   keys are walked in 64-token tiles, tiles dealt round-robin to the waves.
+// * All G query heads of KV head g and all q_len new tokens form the rows of
+//   one MFMA operand (NQB blocks of 16 rows), so every K/V byte is loaded once
+//   per (sequence, KV head) and shared by the whole group.
+// * S^T = K Q^T with v_mfma_f32_16x16x32 (keys on M, query rows on N). Each
+//   lane loads its key rows straight from HBM with 128-bit loads and
+//   dequantizes them in registers; a tile needs no LDS, because no other wave
+//   reads it. Keys are dealt to MFMA rows so that each lane's S^T outputs are
+//   exactly the 16 keys it later feeds as the B operand of O^T += V^T P^T --
+//   P never moves between lanes.
+// * Values are stored dimension-major in each page, so a lane's 16 keys of one
+//   head dimension are 16 contiguous bytes: the A operand of the PV MFMA is one
+//   128-bit load, no transpose.
+// * Online softmax per row in exp2 units; the row max is reduced across the 4
+//   lanes that share a row with two cross-lane exchanges, the row sum stays
+//   lane-partial until the end.
+// * The 4 waves' (m, l, O) are merged through LDS, and each work-group writes
+//   one partial per row; the combine kernel merges the partitions in a fixed
+//   order, so results are bitwise reproducible.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+template <int QT>
+struct QOp { using T = half8; };
+template <>
+struct QOp<Q_BF16> { using T = bf16x8; };
+
+template <int QT>
+__device__ __forceinline__ f32x4 mfma_qk(typename QOp<QT>::T a, typename QOp<QT>::T b, f32x4 c) {
+  if constexpr (QT == Q_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+}
+
+// 8 consecutive key elements (dwords w0, w1 of FP8; or 4 dwords of fp16) as
+// the QK operand type.
+template <int FMT, int QT>
+__device__ __forceinline__ typename QOp<QT>::T key_op(const uint32_t* dw) {
+  if constexpr (FMT == KV_F16) {
+    u32x4 r = {dw[0], dw[1], dw[2], dw[3]};
+    return __builtin_bit_cast(typename QOp<QT>::T, r);  // QT is F16 here
+  } else if constexpr (QT == Q_BF16) {
+    return fp8x8_to_bf16x8<FMT>(dw[0], dw[1]);
+  } else {
+    return fp8x8_to_half8<FMT>(dw[0], dw[1]);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ half8 val_op(const uint32_t* dw) {
+  if constexpr (FMT == KV_F16) {
+    u32x4 r = {dw[0], dw[1], dw[2], dw[3]};
+    return __builtin_bit_cast(half8, r);
+  } else {
+    return fp8x8_to_half8<FMT>(dw[0], dw[1]);
+  }
+}
+
+constexpr float kNegInf = -__builtin_inff();
+
+template <int D, int FMT, int QT, int NQB>
+__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
+  constexpr int ES = (FMT == KV_F16) ? 2 : 1;  // bytes per cache element
+  constexpr int KSTEPS = D / 32;               // MFMA k-steps over the head dim
+  constexpr int RUN = D / 4;                   // key elements per lane per key row
+  constexpr int KDW = RUN * ES / 4;            // dwords per lane per key row
+  constexpr int DB = D / 16;                   // 16-dim blocks of the output
+  constexpr int VDW = 16 * ES / 4;             // dwords per lane per value run
+  using OpT = typename QOp<QT>::T;
+
+  __shared__ float sm_o[4][D][17];
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15;   // MFMA column: query row within a 16-row block
+  const int qg = lane >> 4;  // MFMA k-group
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int rows = a.q_len * G;
+  const int ctx = a.context_lens[b];
+  const int tb = p * a.part_len;
+  const int te = min(tb + a.part_len, ctx);
+  const int ntiles = te > tb ? (te - tb + 63) >> 6 : 0;
+  const int bs_log2 = a.bs_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
+
+  // Query operands (B of S^T = K Q^T): row r = nb*16 + c, head dims
+  // RUN*qg + 8j .. +7 for k-step j. Padding rows are zero.
+  OpT qop[NQB][KSTEPS];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int r = nb * 16 + c;
+    if (r < rows) {
+      const int qi = r / G, h = g * G + r % G;
+      const uint16_t* qp = a.q + ((int64_t)(b * a.q_len + qi) * a.num_q_heads + h) * D + RUN * qg;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) qop[nb][j] = __builtin_bit_cast(OpT, ld16(qp + 8 * j));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) qop[nb][j] = OpT{};
+    }
+  }
+
+  float m[NQB], l[NQB];
+  f32x4 o[NQB][DB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    m[nb] = kNegInf;
+    l[nb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{0, 0, 0, 0};
+  }
+
+  const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
+  const int64_t kv_heads = a.num_kv_heads;
+  const int first_masked = ctx - a.q_len + 1;  // smallest key some row cannot see
+
+  for (int n = w; n < ntiles; n += 4) {
+    const int t0 = tb + (n << 6);
+    const bool need_mask = t0 + 64 > first_masked;
+    const int tk = t0 + 16 * (c >> 2);  // first key of this lane's K group
+    const int tv = t0 + 16 * qg;        // first key of this lane's V group
+    const bool kok = !need_mask || tk < ctx;
+    const bool vok = !need_mask || tv < ctx;
+
+    uint32_t kraw[4][KDW];
+    uint32_t vraw[DB][VDW];
+    if (kok) {
+      const int64_t page = btb[tk >> bs_log2];
+      const uint8_t* kp = a.key_cache +
+          (((page * kv_heads + g) << bs_log2) + (tk & bs_mask) + (c & 3)) * (int64_t)(D * ES) +
+          RUN * qg * ES;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int x = 0; x < KDW / 4; ++x) {
+          u32x4 v = ld16(kp + (int64_t)4 * s * D * ES + 16 * x);
+          kraw[s][4 * x] = v.x; kraw[s][4 * x + 1] = v.y;
+          kraw[s][4 * x + 2] = v.z; kraw[s][4 * x + 3] = v.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int x = 0; x < KDW; ++x) kraw[s][x] = 0;
+    }
+    if (vok) {
+      const int64_t page = btb[tv >> bs_log2];
+      const uint8_t* vp = a.value_cache +
+          ((((page * kv_heads + g) * D + c) << bs_log2) + (tv & bs_mask)) * (int64_t)ES;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int x = 0; x < VDW / 4; ++x) {
+          u32x4 v = ld16(vp + ((int64_t)(db * 16) << bs_log2) * ES + 16 * x);
+          vraw[db][4 * x] = v.x; vraw[db][4 * x + 1] = v.y;
+          vraw[db][4 * x + 2] = v.z; vraw[db][4 * x + 3] = v.w;
+        }
+      }
+      if (need_mask) {
+        // zero the value elements of keys past the context (select, never
+        // multiply: a poisoned slot may hold NaN)
+        const int nvalid = ctx - tv;  // >= 1 here
+        if (nvalid < 16) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (e >= nvalid) {
+#pragma unroll
+              for (int db = 0; db < DB; ++db) {
+                if constexpr (ES == 1) {
+                  vraw[db][e >> 2] &= ~(0xFFu << ((e & 3) * 8));
+                } else {
+                  vraw[db][e >> 1] &= ~(0xFFFFu << ((e & 1) * 16));
+                }
+              }
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < VDW; ++x) vraw[db][x] = 0;
+    }
+
+    // S^T = K Q^T: S-tile s row i of k-group qg holds key t0 + 16 qg + 4 s + i.
+    f32x4 sacc[NQB][4];
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sacc[nb][s] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        OpT kop = key_op<FMT, QT>(&kraw[s][j * (8 * ES / 4)]);
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb) sacc[nb][s] = mfma_qk<QT>(kop, qop[nb][j], sacc[nb][s]);
+      }
+    }
+
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        const int r = nb * 16 + c;
+        const int lim = min(ctx - a.q_len + r / G, ctx - 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + 16 * qg + 4 * s + i > lim) sacc[nb][s][i] = kNegInf;
+      }
+    }
+
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb) {
+      float tm = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sacc[nb][s][i]);
+      tm = fmaxf(tm, lane_xor(tm, 16));
+      tm = fmaxf(tm, lane_xor(tm, 32));
+      const float mnew = fmaxf(m[nb], tm * C);
+      const float muse = mnew == kNegInf ? 0.0f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m[nb] - muse);
+      float ps = 0.0f;
+      half8 pop[2];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nb][s][i], C, -muse));
+          ps += pv;
+          pop[s >> 1][(s & 1) * 4 + i] = (_Float16)pv;
+        }
+      }
+      l[nb] = l[nb] * alpha + ps;
+      m[nb] = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        o[nb][db] *= alpha;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          half8 vop = val_op<FMT>(&vraw[db][hh * (8 * ES / 4)]);
+          o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[hh], o[nb][db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Merge the 4 waves' states for each 16-row block and write one partial per
+  // row: (max, sum) and the unnormalised output, all relative to the max.
+  const int64_t P = a.num_parts;
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    float lf = l[nb];
+    lf += lane_xor(lf, 16);
+    lf += lane_xor(lf, 32);
+    if (qg == 0) {
+      sm_m[w][c] = m[nb];
+      sm_l[w][c] = lf;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[w][db * 16 + 4 * qg + i][c] = o[nb][db][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * D; e += 256) {
+      const int d = e % D, cc = e / D;
+      const int r = nb * 16 + cc;
+      if (r >= rows) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][cc]);
+      float acc = 0.0f, lt = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = sm_m[ww][cc];
+        if (mw == kNegInf) continue;
+        const float wt = __builtin_amdgcn_exp2f(mw - M);
+        acc += wt * sm_o[ww][d][cc];
+        lt += wt * sm_l[ww][cc];
+      }
+      const int qi = r / G, h = g * G + r % G;
+      const int64_t rowg = (int64_t)(b * a.q_len + qi) * a.num_q_heads + h;
+      a.ws_o[(rowg * P + p) * D + d] = acc;
+      if (d == 0) {
+        a.ws_ml[(rowg * P + p) * 2] = M;
+        a.ws_ml[(rowg * P + p) * 2 + 1] = lt;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One wave per output row: out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p,
+// partitions in index order, empty ones (m_p = -inf) left out; times the
+// per-head value scale. A row with no visible key is written as zeros.
+template <int D, int FMT, int OT>
+__global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
+  constexpr int PER = D / 64;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h = (int)(row % a.num_q_heads);
+  const int g = h / G;
+  const int P = a.num_parts;
+  const float* ml = a.ws_ml + row * P * 2;
+  const float* po = a.ws_o + row * P * D;
+  float M = kNegInf;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, ml[2 * p]);
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+  float L = 0.0f;
+  if (M != kNegInf) {
+    for (int p = 0; p < P; ++p) {
+      const float mp = ml[2 * p];
+      if (mp == kNegInf) continue;
+      const float wt = __builtin_amdgcn_exp2f(mp - M);
+      L += wt * ml[2 * p + 1];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] += wt * po[(int64_t)p * D + lane + 64 * k];
+    }
+  }
+  const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
+  const float f = L > 0.0f ? vscale / L : 0.0f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) store_out<OT>(a.out, row * D + lane + 64 * k, acc[k] * f);
+}
+
+template <int D, int FMT, int QT, int NQB>
+static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
+  dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
+  hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB>), grid, dim3(256), 0, stream, a);
+}
+
+template <int D, int FMT, int QT>
+static void launch_split_nqb(const DecodeArgs& a, int batch, int nqb, hipStream_t stream) {
+  if (nqb == 1) launch_split<D, FMT, QT, 1>(a, batch, stream);
+  else if (nqb == 2) launch_split<D, FMT, QT, 2>(a, batch, stream);
+  else launch_split<D, FMT, QT, 4>(a, batch, stream);
+}
+
+template <int D, int FMT>
+static void launch_combine(const DecodeArgs& a, int64_t rows, int ot, hipStream_t stream) {
+  dim3 grid((unsigned)rows), block(64);
+  if (ot == O_F32) hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_F32>), grid, block, 0, stream, a);
+  else if (ot == O_F16) hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_F16>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_BF16>), grid, block, 0, stream, a);
+}
+
+template <int D>
+static void launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int ot, int nqb,
+                            hipStream_t stream) {
+  if (fmt == KV_F16) {
+    launch_split_nqb<D, KV_F16, Q_F16>(a, batch, nqb, stream);
+  } else if (fmt == KV_E4M3) {
+    if (qt == Q_BF16) launch_split_nqb<D, KV_E4M3, Q_BF16>(a, batch, nqb, stream);
+    else launch_split_nqb<D, KV_E4M3, Q_F16>(a, batch, nqb, stream);
+  } else {
+    if (qt == Q_BF16) launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream);
+    else launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream);
+  }
+  const int64_t rows = (int64_t)batch * a.q_len * a.num_q_heads;
+  if (fmt == KV_F16) launch_combine<D, KV_F16>(a, rows, ot, stream);
+  else if (fmt == KV_E4M3) launch_combine<D, KV_E4M3>(a, rows, ot, stream);
+  else launch_combine<D, KV_E5M2>(a, rows, ot, stream);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int batch, int head_dim, int fmt, int qt, int ot,
+                         int nqb, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  if (head_dim == 64) launch_decode_d<64>(a, batch, fmt, qt, ot, nqb, stream);
+  else launch_decode_d<128>(a, batch, fmt, qt, ot, nqb, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,317 @@
+// Causal chunked prefill over the block-paged KV cache.
+//
+// What the pages describe ("SM70 release profile and acceleration status":
+// prompts prefilled in 4096-token chunks, each chunk attending to the pages
+// written so far; "1Cat-vLLM 1.5.0" RELEASE notes, "Flash-V100 long-context
+// improvements": a long-prefill GQA kernel with FP32 accumulation that packs
+// several query heads onto one KV head's tensor-core work, measured in
+// useful causal FLOP/s). How it is done here (gfx950):
+//
+// * Work-group = 128 rows that share one KV head: 128/G query tokens x the G
+//   query heads of that KV head (GQA packing), 4 waves x 32 rows.
+// * The grid is ordered so that consecutive work-groups take consecutive KV
+//   heads: with round-robin dispatch over the 8 XCDs, each XCD's L2 holds the
+//   K/V of one head while all its work-groups stream it. Query tiles with the
+//   most keys are dispatched first.
+// * Keys are walked in 64-key tiles. 256 threads load the FP8 tile with
+//   128-bit loads (page id per 16-key run), dequantize in registers and store
+//   16-bit K (token-major) and V (dimension-major) tiles in LDS, double
+//   buffered, one barrier per tile; the next tile's global loads are in
+//   flight while the current tile is multiplied.
+// * S^T = K Q^T on v_mfma_f32_32x32x16 (keys on M, query rows on N, Q held in
+//   registers), FP32 accumulation. Keys are assigned to MFMA rows with bits 2
+//   and 3 of the row index swapped, which makes each lane's S^T outputs the
+//   8-key runs that the PV step needs as its B operand: P never leaves the
+//   lane, and the V^T operand is one 16-byte LDS read.
+// * Online softmax in exp2 units, the row max reduced between the two lanes
+//   that share a row; only tiles that cross the causal diagonal are masked.
+// * P is rounded to fp16 (V from FP8 is exact in fp16) and O^T += V^T P^T runs
+//   on v_mfma_f32_32x32x16_f16.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+template <int QT>
+struct QOp32 { using T = half8; };
+template <>
+struct QOp32<Q_BF16> { using T = bf16x8; };
+
+template <int QT>
+__device__ __forceinline__ f32x16 mfma32_qk(typename QOp32<QT>::T a, typename QOp32<QT>::T b,
+                                            f32x16 c) {
+  if constexpr (QT == Q_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+}
+
+constexpr float kNegInfP = -__builtin_inff();
+
+// MFMA row R of a 32-key block holds key kappa(R): bits 2 and 3 swapped.
+__device__ __forceinline__ int kappa(int R) {
+  return (R & ~12) | ((R & 4) << 1) | ((R & 8) >> 1);
+}
+
+template <int D, int FMT, int QT, int OT>
+__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+  constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  constexpr int BN = 64;                  // keys per tile
+  constexpr int KPAD = D + 8;             // K tile row stride (16-bit elements)
+  constexpr int VPAD = BN + 8;            // V tile row stride
+  constexpr int KS = D / 16;              // QK k-steps (16 dims each)
+  constexpr int DBLK = D / 32;            // 32-dim output blocks
+  constexpr int EPT = D / 4;              // elements per thread per tile (K and V)
+  constexpr int TPR = 256 / D;            // threads per V row (dimension)
+  using OpT = typename QOp32<QT>::T;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][BN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * VPAD];
+
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int TOK = kPrefillRows / G;       // query tokens per work-group
+  int idx = blockIdx.x;
+  const int g = idx % Hkv;
+  idx /= Hkv;
+  const int qb = a.q_blocks - 1 - (idx % a.q_blocks);  // heavy tiles first
+  const int b = idx / a.q_blocks;
+
+  const int q0 = a.cu_seqlens[b];
+  const int qlen = a.cu_seqlens[b + 1] - q0;
+  const int tok0 = qb * TOK;
+  if (tok0 >= qlen) return;
+  const int ntok = min(TOK, qlen - tok0);
+  const int ctx = a.context_lens[b];
+  const int first_pos = ctx - qlen + tok0;          // position of the first row token
+  const int last_pos = first_pos + ntok - 1;
+  const int ntiles = last_pos / BN + 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, hgrp = lane >> 5;
+  const int bs_log2 = a.bs_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
+  const int64_t kvh = Hkv;
+
+  const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
+
+  // This lane's query row (MFMA column): r = 32 w + c32 -> (token, head).
+  const int r = w * 32 + c32;
+  const int rtok = r / G, rh = g * G + r % G;
+  const bool rvalid = rtok < ntok;
+  const int rpos = first_pos + rtok;
+  OpT qop[KS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)(q0 + tok0 + rtok) * a.num_q_heads + rh) * D + 8 * hgrp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[ks] = rvalid ? __builtin_bit_cast(OpT, ld16(qp + 16 * ks)) : OpT{};
+  }
+
+  // ---- global -> register staging of one tile ----
+  // K: thread owns key kt = tid / 4, dims kd0 .. kd0 + EPT - 1.
+  // V: thread owns dim vd = tid / TPR, keys vk0 .. vk0 + EPT - 1.
+  const int kt = tid >> 2, kd0 = (tid & 3) * EPT;
+  const int vd = tid / TPR, vk0 = (tid % TPR) * EPT;
+  constexpr int KLD = EPT * ES / 16;      // 16-byte loads for K
+  constexpr int VLD = EPT * ES / 16;      // 16-byte loads for V
+  u32x4 kreg[KLD], vreg[VLD];
+
+  auto load_tile = [&](int t0) {
+    const int key = t0 + kt;
+    if (key < ctx) {
+      const int64_t page = btb[key >> bs_log2];
+      const uint8_t* kp = a.key_cache +
+          (((page * kvh + g) << bs_log2) + (key & bs_mask)) * (int64_t)(D * ES) + kd0 * ES;
+#pragma unroll
+      for (int x = 0; x < KLD; ++x) kreg[x] = ld16(kp + 16 * x);
+    } else {
+#pragma unroll
+      for (int x = 0; x < KLD; ++x) kreg[x] = u32x4{0, 0, 0, 0};
+    }
+    // V: each 16-byte load covers 16 / ES consecutive keys of dimension vd
+    constexpr int KPL = 16 / ES;
+#pragma unroll
+    for (int x = 0; x < VLD; ++x) {
+      const int k0 = t0 + vk0 + x * KPL;
+      if (k0 < ctx) {
+        const int64_t page = btb[k0 >> bs_log2];
+        const uint8_t* vp = a.value_cache +
+            ((((page * kvh + g) * D + vd) << bs_log2) + (k0 & bs_mask)) * (int64_t)ES;
+        u32x4 v = ld16(vp);
+        const int nvalid = ctx - k0;
+        if (nvalid < KPL) {
+          // zero elements of keys past the context (select; slots may be NaN)
+          uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) {
+            if (i >= nvalid) {
+              if constexpr (ES == 1) e[i >> 2] &= ~(0xFFu << ((i & 3) * 8));
+              else e[i >> 1] &= ~(0xFFFFu << ((i & 1) * 16));
+            }
+          }
+          v = u32x4{e[0], e[1], e[2], e[3]};
+        }
+        vreg[x] = v;
+      } else {
+        vreg[x] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* kdst = &sk[buf][kt * KPAD + kd0];
+    uint16_t* vdst = &sv[buf][vd * VPAD + vk0];
+    if constexpr (FMT == KV_F16) {
+#pragma unroll
+      for (int x = 0; x < KLD; ++x) *reinterpret_cast<u32x4*>(kdst + 8 * x) = kreg[x];
+#pragma unroll
+      for (int x = 0; x < VLD; ++x) *reinterpret_cast<u32x4*>(vdst + 8 * x) = vreg[x];
+    } else {
+#pragma unroll
+      for (int x = 0; x < KLD; ++x) {
+        if constexpr (QT == Q_BF16) {
+          *reinterpret_cast<bf16x8*>(kdst + 16 * x) = fp8x8_to_bf16x8<FMT>(kreg[x].x, kreg[x].y);
+          *reinterpret_cast<bf16x8*>(kdst + 16 * x + 8) = fp8x8_to_bf16x8<FMT>(kreg[x].z, kreg[x].w);
+        } else {
+          *reinterpret_cast<half8*>(kdst + 16 * x) = fp8x8_to_half8<FMT>(kreg[x].x, kreg[x].y);
+          *reinterpret_cast<half8*>(kdst + 16 * x + 8) = fp8x8_to_half8<FMT>(kreg[x].z, kreg[x].w);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < VLD; ++x) {
+        *reinterpret_cast<half8*>(vdst + 16 * x) = fp8x8_to_half8<FMT>(vreg[x].x, vreg[x].y);
+        *reinterpret_cast<half8*>(vdst + 16 * x + 8) = fp8x8_to_half8<FMT>(vreg[x].z, vreg[x].w);
+      }
+    }
+  };
+
+  float m = kNegInfP, l = 0.0f;
+  f32x16 oacc[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+
+  const int krow0 = kappa(c32);  // K tile row this lane feeds for MFMA row c32
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    const int t0 = n * BN;
+    if (n + 1 < ntiles) load_tile(t0 + BN);
+
+    const uint16_t* skb = sk[buf];
+    const uint16_t* svb = sv[buf];
+
+    // S^T = K Q^T for two 32-key blocks.
+    f32x16 sacc[2];
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        OpT kop = *reinterpret_cast<const OpT*>(skb + (mb * 32 + krow0) * KPAD + 16 * ks + 8 * hgrp);
+        sacc[mb] = mfma32_qk<QT>(kop, qop[ks], sacc[mb]);
+      }
+    }
+
+    // Keys held by this lane: block mb, register j -> MFMA row
+    // R = 8 (j/4) + 4 hgrp + j%4 -> key t0 + 32 mb + kappa(R)
+    //   = t0 + 32 mb + 16 (j/8) + 8 hgrp + 4 ((j/4)&1) + j%4.
+    if (t0 + BN - 1 > first_pos) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = t0 + 32 * mb + 16 * (j >> 3) + 8 * hgrp + 4 * ((j >> 2) & 1) + (j & 3);
+          if (key > rpos || key >= ctx) sacc[mb][j] = kNegInfP;
+        }
+    }
+
+    float tm = kNegInfP;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sacc[mb][j]);
+    tm = fmaxf(tm, lane_xor(tm, 32));
+    const float mnew = fmaxf(m, tm * C);
+    const float muse = mnew == kNegInfP ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - muse);
+    m = mnew;
+    float ps = 0.0f;
+    half8 pop[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][j], C, -muse));
+        ps += pv;
+        pop[mb * 2 + (j >> 3)][j & 7] = (_Float16)pv;
+      }
+    l = l * alpha + ps;
+
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      oacc[db] *= alpha;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        half8 vop = *reinterpret_cast<const half8*>(svb + (db * 32 + c32) * VPAD + 16 * kk + 8 * hgrp);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[kk], oacc[db], 0, 0, 0);
+      }
+    }
+
+    if (n + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r].
+  l += lane_xor(l, 32);
+  if (!rvalid) return;
+  const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
+  const float f = l > 0.0f ? vscale / l : 0.0f;
+  const int64_t obase = ((int64_t)(q0 + tok0 + rtok) * a.num_q_heads + rh) * D;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int d = 32 * db + 8 * (j >> 2) + 4 * hgrp + (j & 3);
+      store_out<OT>(a.out, obase + d, oacc[db][j] * f);
+    }
+}
+
+template <int D, int FMT, int QT>
+static void launch_pf(const PrefillArgs& a, int ot, hipStream_t s) {
+  const unsigned nblk = (unsigned)((int64_t)a.num_kv_heads * a.q_blocks * a.batch);
+  dim3 grid(nblk), block(256);
+  if (ot == O_F32) hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_F32>), grid, block, 0, s, a);
+  else if (ot == O_F16) hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_F16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_BF16>), grid, block, 0, s, a);
+}
+
+template <int D>
+static void launch_pf_d(const PrefillArgs& a, int fmt, int qt, int ot, hipStream_t s) {
+  if (fmt == KV_F16) launch_pf<D, KV_F16, Q_F16>(a, ot, s);
+  else if (fmt == KV_E4M3) {
+    if (qt == Q_BF16) launch_pf<D, KV_E4M3, Q_BF16>(a, ot, s);
+    else launch_pf<D, KV_E4M3, Q_F16>(a, ot, s);
+  } else {
+    if (qt == Q_BF16) launch_pf<D, KV_E5M2, Q_BF16>(a, ot, s);
+    else launch_pf<D, KV_E5M2, Q_F16>(a, ot, s);
+  }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int fmt, int qt, int ot,
+                          hipStream_t stream) {
+  if (a.batch == 0 || a.q_blocks == 0) return hipSuccess;
+  if (head_dim == 64) launch_pf_d<64>(a, fmt, qt, ot, stream);
+  else launch_pf_d<128>(a, fmt, qt, ot, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pa

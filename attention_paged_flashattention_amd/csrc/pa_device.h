@@ -1,0 +1,178 @@
+// Device-side helpers shared by the paged-attention kernels (gfx950 only).
+//
+// FP8 formats are OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN) and E5M2
+// (bias 15, max 57344), the two KV-cache formats of "1Cat-vLLM 1.0.0" README,
+// "Optional experimental feature: FP8 KV cache".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Cache element formats (compile-time tags).
+enum KvFmt : int { KV_F16 = 0, KV_E4M3 = 1, KV_E5M2 = 2 };
+// Query element types.
+enum QType : int { Q_F16 = 0, Q_BF16 = 1 };
+// Output element types.
+enum OType : int { O_F32 = 0, O_F16 = 1, O_BF16 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// FP8 -> 16-bit, exact, integer only.
+//
+// E5M2 is the upper byte of an fp16 with the same exponent bias, so
+// half_bits = code << 8 is the value itself.
+//
+// E4M3: half_bits = (code & 0x7F) << 7 | sign << 15 puts the 4 exponent and
+// 3 mantissa bits under fp16's 5-bit exponent (bias 15 instead of 7), which
+// is the code's value times 2^-8 exactly -- subnormal codes land on fp16
+// subnormals m * 2^-17 -- so the 2^8 is folded into the per-head scale.
+// The NaN code 0x7F maps to the finite 1.875; the write kernel never stores
+// it for finite inputs, and masked cache slots never reach the arithmetic.
+// ---------------------------------------------------------------------------
+constexpr float kE4m3Fold = 256.0f;
+
+// Two bytes (b0, b1) of w selected by `sel` (a v_perm_b32 selector that places
+// them in the high byte of each 16-bit half) -> two fp16 bit patterns.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8x2_to_h2(uint32_t w, uint32_t sel) {
+  uint32_t u = __builtin_amdgcn_perm(0u, w, sel);  // (b1 << 24) | (b0 << 8)
+  if constexpr (FMT == KV_E5M2) {
+    return u;
+  } else {
+    return ((u >> 1) & 0x3F803F80u) | (u & 0x80008000u);
+  }
+}
+
+// 4 FP8 codes in a dword -> 4 fp16 (2 dwords), element order preserved.
+template <int FMT>
+__device__ __forceinline__ u32x2 fp8x4_to_h4(uint32_t w) {
+  u32x2 r;
+  r.x = fp8x2_to_h2<FMT>(w, 0x010c000cu);  // bytes 0,1
+  r.y = fp8x2_to_h2<FMT>(w, 0x030c020cu);  // bytes 2,3
+  return r;
+}
+
+// 8 FP8 codes (2 dwords) -> half8 MFMA operand.
+template <int FMT>
+__device__ __forceinline__ half8 fp8x8_to_half8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  u32x2 a = fp8x4_to_h4<FMT>(w0);
+  u32x2 b = fp8x4_to_h4<FMT>(w1);
+  r.x = a.x; r.y = a.y; r.z = b.x; r.w = b.y;
+  return __builtin_bit_cast(half8, r);
+}
+
+// Two fp16 bit patterns -> two bf16 bit patterns. Exact for every value an
+// FP8 code produces (at most 4 significant bits, exponents far inside bf16's
+// range): fp16 -> fp32 is exact and the low 16 bits of the fp32 are zero.
+__device__ __forceinline__ uint32_t h2_to_bf2(uint32_t h2) {
+  _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(h2 & 0xFFFFu));
+  _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(h2 >> 16));
+  uint32_t flo = __builtin_bit_cast(uint32_t, (float)lo);
+  uint32_t fhi = __builtin_bit_cast(uint32_t, (float)hi);
+  return __builtin_amdgcn_perm(fhi, flo, 0x07060302u);  // high halves
+}
+
+template <int FMT>
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x2 a = fp8x4_to_h4<FMT>(w0);
+  u32x2 b = fp8x4_to_h4<FMT>(w1);
+  u32x4 r;
+  r.x = h2_to_bf2(a.x); r.y = h2_to_bf2(a.y);
+  r.z = h2_to_bf2(b.x); r.w = h2_to_bf2(b.y);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Factor that turns the 16-bit operand value back into the code's value.
+template <int FMT>
+__device__ __forceinline__ constexpr float kv_fold() {
+  return FMT == KV_E4M3 ? kE4m3Fold : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> FP8, saturating, round to nearest even. Integer rounding of the
+// fp32 bit pattern for normals; rint of an exact power-of-two rescale in the
+// subnormal range. The sign bit is always kept.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  uint32_t u = __builtin_bit_cast(uint32_t, y);
+  uint32_t s = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return s | 0x7Fu;            // NaN
+  if (a >= 0x43E00000u) return s | 0x7Eu;           // >= 448 (and inf): saturate
+  if (a < 0x3C800000u) {                            // < 2^-6: quantum 2^-9
+    float f = __builtin_bit_cast(float, a) * 512.0f;
+    return s | (uint32_t)__builtin_rintf(f);        // 0..8 (8 = smallest normal)
+  }
+  uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);     // RNE to 3 mantissa bits
+  return s | ((r >> 20) - (120u << 3));
+}
+
+__device__ __forceinline__ uint32_t f32_to_e5m2(float y) {
+  uint32_t u = __builtin_bit_cast(uint32_t, y);
+  uint32_t s = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return s | 0x7Fu;            // NaN
+  if (a >= 0x47600000u) return s | 0x7Bu;           // >= 57344 (and inf): saturate
+  if (a < 0x38800000u) {                            // < 2^-14: quantum 2^-16
+    float f = __builtin_bit_cast(float, a) * 65536.0f;
+    return s | (uint32_t)__builtin_rintf(f);        // 0..4
+  }
+  uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);     // RNE to 2 mantissa bits
+  return s | ((r >> 21) - (112u << 2));
+}
+
+// 16-bit source element -> fp32 (exact).
+template <int ST>
+__device__ __forceinline__ float src_to_f32(uint16_t bits) {
+  if constexpr (ST == Q_BF16) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Output stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int OT>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+  if constexpr (OT == O_F32) {
+    reinterpret_cast<float*>(out)[idx] = v;
+  } else if constexpr (OT == O_F16) {
+    reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Global loads of 16 bytes with no alias assumptions.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace pa

@@ -1,0 +1,76 @@
+// Host-side internal interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct WriteArgs {
+  const uint16_t* key;
+  const uint16_t* value;
+  const int64_t* slots;
+  int64_t num_tokens;
+  uint8_t* key_cache;
+  uint8_t* value_cache;
+  const float* k_scale;  // may be null (E5M2 without scales, F16)
+  const float* v_scale;
+  int num_kv_heads;
+  int head_dim;
+  int bs_log2;
+};
+
+// Split-KV decode / grouped verify.
+struct DecodeArgs {
+  const uint16_t* q;        // [batch][q_len][Hq][D]
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* k_scale;
+  const float* v_scale;
+  float* ws_ml;             // [rows][P][2]  (running max in log2 units, sum)
+  float* ws_o;              // [rows][P][D]  (unnormalised partial output)
+  void* out;                // [rows][D]
+  int max_blocks;
+  int q_len;
+  int num_q_heads;
+  int num_kv_heads;
+  int bs_log2;
+  int part_len;             // tokens per partition, a multiple of 64
+  int num_parts;
+  float softmax_scale;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;        // [total_q][Hq][D]
+  const int32_t* cu_seqlens;
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* k_scale;
+  const float* v_scale;
+  void* out;                // [total_q][Hq][D]
+  int batch;
+  int max_blocks;
+  int num_q_heads;
+  int num_kv_heads;
+  int bs_log2;
+  int q_blocks;             // query tiles per sequence in the grid
+  float softmax_scale;
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream);
+
+// fmt: KvFmt, qt: QType, ot: OType. nqb: number of 16-row query blocks.
+hipError_t launch_decode(const DecodeArgs& a, int batch, int head_dim, int fmt, int qt,
+                         int ot, int nqb, hipStream_t stream);
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int fmt, int qt, int ot,
+                          hipStream_t stream);
+
+// Rows of the prefill work-group tile (query tokens x heads of one KV group).
+constexpr int kPrefillRows = 128;
+
+}  // namespace pa

@@ -1,0 +1,206 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+symbol include/pagedattn.h declares, and rejects bad arguments with the exact
+status code before anything is launched."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+
+@pytest.fixture(scope="module")
+def pa():
+    from attention_paged_flashattention_amd import pagedattn
+    return pagedattn
+
+
+def _declared():
+    src = open(HEADER).read()
+    return re.findall(r"PA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_header_declares_the_four_operations():
+    names = _declared()
+    for n in ["kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged", "attn_verify_paged"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(pa):
+    names = _declared()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(pa.lib(), n)
+    assert set(pa.EXPORTS) == set(names)
+
+
+def test_version(pa):
+    assert "gfx950" in pa.pa_version()
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+NUL = None
+
+
+def _decode_args(**kw):
+    a = dict(q=FAKE, q_dtype=0, batch=2, kc=FAKE, vc=FAKE, cache_dtype=3, bs=16, nb=10, bt=FAKE,
+             maxblk=4, ctx=FAKE, maxctx=64, hq=8, hkv=2, d=128, ks=FAKE, vs=FAKE, scale=0.125,
+             parts=0, ws=FAKE, wsb=1 << 20, out=FAKE, out_dtype=2, stream=NUL)
+    a.update(kw)
+    return a
+
+
+def _call_decode(pa, **kw):
+    a = _decode_args(**kw)
+    return pa.lib().attn_decode_paged(a["q"], a["q_dtype"], a["batch"], a["kc"], a["vc"],
+                                      a["cache_dtype"], a["bs"], a["nb"], a["bt"], a["maxblk"],
+                                      a["ctx"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["ks"],
+                                      a["vs"], a["scale"], a["parts"], a["ws"], a["wsb"], a["out"],
+                                      a["out_dtype"], a["stream"])
+
+
+def _call_verify(pa, q_len, **kw):
+    a = _decode_args(**kw)
+    return pa.lib().attn_verify_paged(a["q"], a["q_dtype"], a["batch"], q_len, a["kc"], a["vc"],
+                                      a["cache_dtype"], a["bs"], a["nb"], a["bt"], a["maxblk"],
+                                      a["ctx"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["ks"],
+                                      a["vs"], a["scale"], a["parts"], a["ws"], a["wsb"], a["out"],
+                                      a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NUL), 1),
+    (dict(kc=NUL), 1),
+    (dict(bt=NUL), 1),
+    (dict(out=NUL), 1),
+    (dict(hq=7, hkv=2), 1),
+    (dict(hkv=0), 1),
+    (dict(d=0), 1),
+    (dict(d=96), 2),
+    (dict(d=256), 2),
+    (dict(bs=24), 2),
+    (dict(bs=8, maxctx=32), 2),
+    (dict(bs=0), 1),
+    (dict(q_dtype=2), 2),
+    (dict(cache_dtype=1), 2),
+    (dict(cache_dtype=0, q_dtype=1), 2),
+    (dict(out_dtype=3), 2),
+    (dict(ks=NUL), 1),
+    (dict(vs=NUL), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=-1.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(maxctx=65), 1),           # > max_blocks * block_size
+    (dict(maxctx=-1), 1),
+    (dict(batch=-1), 1),
+    (dict(parts=-2), 1),
+    (dict(parts=5000), 2),
+    (dict(ws=NUL), 1),
+    (dict(wsb=16), 1),
+    (dict(ws=ctypes.c_void_p(0x1010)), 1),   # misaligned workspace
+    (dict(hq=128, hkv=1), 2),                # G = 128 rows exceed one decode group
+])
+def test_decode_rejects_before_launch(pa, kw, status):
+    assert _call_decode(pa, **kw) == status
+    assert pa.pa_last_error() != ""
+
+
+def test_e5m2_needs_no_scales_and_batch_zero_is_a_noop(pa):
+    # passes validation and returns before any launch because batch == 0
+    assert _call_decode(pa, batch=0, cache_dtype=4, ks=NUL, vs=NUL) == 0
+    assert pa.pa_last_error() == ""
+
+
+def test_verify_limits(pa):
+    assert _call_verify(pa, 0) == 1
+    assert _call_verify(pa, 17, hq=8, hkv=2) == 2        # 17 * 4 rows > 64
+    assert _call_verify(pa, 8, batch=0) == 0
+
+
+def test_write_rejects_before_launch(pa):
+    L = pa.lib()
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, src=0, slots=FAKE, T=10, kc=FAKE, vc=FAKE, cdt=3, nb=4, bs=16,
+                 hkv=2, d=128, ks=FAKE, vs=FAKE, stream=NUL)
+        a.update(kw)
+        return L.kv_cache_write_fp8(a["k"], a["v"], a["src"], a["slots"], a["T"], a["kc"], a["vc"],
+                                    a["cdt"], a["nb"], a["bs"], a["hkv"], a["d"], a["ks"], a["vs"],
+                                    a["stream"])
+    assert call(T=-1) == 1
+    assert call(k=NUL) == 1
+    assert call(slots=NUL) == 1
+    assert call(src=2) == 2
+    assert call(cdt=1) == 2
+    assert call(cdt=0, src=1) == 2
+    assert call(ks=NUL) == 1
+    assert call(d=40) == 2
+    assert call(bs=48) == 2
+    assert call(nb=0) == 1
+    assert call(T=0) == 0                       # no-op, nothing launched
+    assert call(T=0, cdt=4, ks=NUL, vs=NUL) == 0
+
+
+def test_prefill_rejects_before_launch(pa):
+    L = pa.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, qdt=1, cu=FAKE, B=1, maxq=64, totq=64, kc=FAKE, vc=FAKE, cdt=3, bs=2048,
+                 nb=4, bt=FAKE, maxblk=2, ctx=FAKE, maxctx=4096, hq=32, hkv=8, d=128, ks=FAKE,
+                 vs=FAKE, scale=0.088, out=FAKE, odt=2, stream=NUL)
+        a.update(kw)
+        return L.attn_prefill_paged(a["q"], a["qdt"], a["cu"], a["B"], a["maxq"], a["totq"], a["kc"],
+                                    a["vc"], a["cdt"], a["bs"], a["nb"], a["bt"], a["maxblk"],
+                                    a["ctx"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["ks"],
+                                    a["vs"], a["scale"], a["out"], a["odt"], a["stream"])
+    assert call(cu=NUL) == 1
+    assert call(maxq=5000) == 1
+    assert call(hq=24, hkv=8) == 2           # G = 3 is not a power of two
+    assert call(hq=64, hkv=1) == 2           # G = 64 > 32
+    assert call(B=-1) == 1
+    assert call(B=0) == 0
+    assert call(totq=0) == 0
+
+
+def test_supports_table(pa):
+    s = pa.pa_supports
+    E4, E5, F16, BF16 = pa.PA_FP8_E4M3, pa.PA_FP8_E5M2, pa.PA_F16, pa.PA_BF16
+    assert s(pa.PA_OP_DECODE, F16, E4, 128, 32, 8, 16, 1)
+    assert s(pa.PA_OP_DECODE, F16, E4, 128, 32, 8, 2048, 1)
+    assert s(pa.PA_OP_VERIFY, F16, E5, 128, 32, 8, 2048, 8)
+    assert s(pa.PA_OP_VERIFY, F16, E5, 128, 32, 8, 2048, 16)
+    assert not s(pa.PA_OP_VERIFY, F16, E5, 128, 32, 8, 2048, 17)
+    assert s(pa.PA_OP_PREFILL, BF16, E4, 128, 32, 8, 2048, 4096)
+    assert s(pa.PA_OP_PREFILL, F16, F16, 64, 4, 1, 16, 64)
+    assert not s(pa.PA_OP_PREFILL, BF16, F16, 64, 4, 1, 16, 64)
+    assert not s(pa.PA_OP_DECODE, F16, E4, 96, 32, 8, 16, 1)
+    assert not s(pa.PA_OP_DECODE, F16, E4, 128, 32, 8, 24, 1)
+    assert s(pa.PA_OP_WRITE, BF16, E4, 128, 8, 8, 2048, 0)
+    assert not s(pa.PA_OP_WRITE, BF16, F16, 128, 8, 8, 2048, 0)
+
+
+def test_partitions_and_workspace(pa):
+    # 128K and 256K single-sequence decode: 64 partitions of 2048 / 4096 keys
+    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 131072) == 64
+    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 262144) == 64
+    assert pa.pa_decode_partitions(8, 1, 32, 8, 128, 4096) == 8
+    assert pa.pa_decode_partitions(4, 8, 32, 8, 128, 131072) == 16
+    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 100) == 1
+    rows, parts, d = 32, 64, 128
+    ml = rows * parts * 2 * 4
+    want = (ml + 255) // 256 * 256 + rows * parts * d * 4
+    assert pa.pa_workspace_bytes(pa.PA_OP_DECODE, 1, 1, 32, 8, 128, 64, 131072) == want
+    assert pa.pa_workspace_bytes(pa.PA_OP_DECODE, 1, 1, 32, 8, 128, 0, 131072) == want
+    assert pa.pa_workspace_bytes(pa.PA_OP_PREFILL, 1, 4096, 32, 8, 128, 0, 32768) == 0
+    assert pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 16, 131072) == \
+        (4 * 8 * 32 * 16 * 2 * 4 + 255) // 256 * 256 + 4 * 8 * 32 * 16 * 128 * 4

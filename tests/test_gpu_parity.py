@@ -1,0 +1,278 @@
+"""GPU parity of every entry point against the float64 CPU oracle, at sizes the
+oracle finishes in seconds: several tiles, ragged tails, both page sizes, all
+cache formats. Calls go through the C ABI (via the ctypes binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+from attention_paged_flashattention_amd import synth
+from oracle import fp8, paged
+from tests.gpu_helpers import check_close, log, oracle_full
+from tests.oracle_helpers import oracle_cache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def runner():
+    from attention_paged_flashattention_amd import runner as r
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return r
+
+
+def _mk(fmt, B, ctx, q_len, Hq=8, Hkv=2, D=128, bs=16, q_dtype="f16", seed=11, sigma_kv=1.0,
+        outlier=0.0):
+    kv_dtype = "bf16" if (q_dtype == "bf16" and fmt != "f16") else "f16"
+    return synth.make_case(f"{fmt}-B{B}-q{q_len}-D{D}-bs{bs}", seed, list(ctx), q_len, Hq, Hkv, D,
+                           bs, q_dtype, kv_dtype, fmt, sigma_kv=sigma_kv, outlier_frac=outlier)
+
+
+def _cache_np(t):
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# quantize-on-write: bit-exact against the oracle, whole caches compared
+# ---------------------------------------------------------------------------
+
+WRITE_CASES = [
+    ("e4m3", "f16", 16, 128, (37, 100, 5)),
+    ("e4m3", "bf16", 2048, 128, (3000,)),
+    ("e5m2", "f16", 64, 64, (130, 17)),
+    ("e5m2", "bf16", 32, 128, (77,)),
+    ("f16", "f16", 16, 64, (65, 33)),
+]
+
+
+@pytest.mark.parametrize("fmt,src,bs,D,ctx", WRITE_CASES)
+def test_write_bit_exact(runner, fmt, src, bs, D, ctx):
+    log(f"write {fmt} src={src} bs={bs} D={D} ctx={ctx}")
+    case = synth.make_case("w", 21, list(ctx), 1, 4, 2, D, bs, "f16", src, fmt,
+                           outlier_frac=0.05)
+    # skip some tokens with a negative slot: they must not be written
+    case.slot_mapping = case.slot_mapping.copy()
+    case.slot_mapping[::7] = -1
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    torch.cuda.synchronize()
+    kc, vc = oracle_cache(case)
+    assert np.array_equal(_cache_np(dc.key_cache).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(_cache_np(dc.value_cache).view(np.uint8), vc.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt,scale", [("e4m3", 1.0), ("e4m3", 0.0105), ("e4m3", 7.0),
+                                       ("e5m2", None), ("e5m2", 0.37)])
+def test_write_every_fp16_pattern(runner, fmt, scale):
+    """All 65536 fp16 bit patterns (NaN and inf included) through the write."""
+    from attention_paged_flashattention_amd import pagedattn as pa
+    log(f"write all fp16 patterns {fmt} scale={scale}")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16).copy()
+    x[np.isnan(x)] = 0          # NaN inputs are outside the contract (sign of NaN unspecified)
+    x = x.reshape(512, 1, 128)
+    T, D, bs = 512, 128, 16
+    nb = T // bs
+    slots = np.arange(T, dtype=np.int64)
+    dev = "cuda:0"
+    k = torch.from_numpy(x.copy()).to(dev)
+    v = torch.from_numpy(x[::-1].copy()).to(dev)
+    kc = torch.full((nb, 1, bs, D), 0x7F, dtype=torch.uint8, device=dev)
+    vc = torch.full((nb, 1, D, bs), 0x7F, dtype=torch.uint8, device=dev)
+    sc = None if scale is None else torch.tensor([scale], dtype=torch.float32, device=dev)
+    pa.kv_cache_write_fp8(k, v, torch.from_numpy(slots).to(dev), kc, vc, fmt, sc, sc)
+    torch.cuda.synchronize()
+    okc, ovc = paged.new_caches(nb, 1, bs, D, fmt, fill=0x7F)
+    s = None if scale is None else np.array([scale], dtype=np.float32)
+    paged.write(x.astype(np.float32), x[::-1].astype(np.float32), slots, okc, ovc, fmt, s, s)
+    assert np.array_equal(kc.cpu().numpy(), okc)
+    assert np.array_equal(vc.cpu().numpy(), ovc)
+
+
+# ---------------------------------------------------------------------------
+# decode and verify
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # fmt, B, ctx, Hq, Hkv, D, bs, q_dtype, partitions
+    ("e4m3", 3, (1, 700, 1500), 32, 8, 128, 16, "f16", 0),
+    ("e4m3", 2, (64, 1000), 32, 8, 128, 16, "f16", 3),
+    ("e4m3", 1, (4097,), 32, 8, 128, 2048, "f16", 1),
+    ("e4m3", 1, (5000,), 32, 8, 128, 2048, "f16", 7),
+    ("e5m2", 2, (300, 2049), 32, 8, 128, 2048, "f16", 0),
+    ("e4m3", 2, (129, 777), 32, 8, 128, 32, "bf16", 0),
+    ("e5m2", 2, (129, 777), 16, 1, 128, 64, "bf16", 5),
+    ("f16", 2, (65, 300), 4, 1, 64, 16, "f16", 0),
+    ("f16", 1, (1000,), 8, 8, 64, 16, "f16", 4),
+    ("e4m3", 2, (100, 513), 8, 2, 64, 16, "f16", 2),
+]
+
+
+@pytest.mark.parametrize("fmt,B,ctx,Hq,Hkv,D,bs,q_dtype,parts", DECODE_CASES)
+def test_decode_parity(runner, fmt, B, ctx, Hq, Hkv, D, bs, q_dtype, parts):
+    log(f"decode {fmt} B={B} ctx={ctx} Hq={Hq} Hkv={Hkv} D={D} bs={bs} q={q_dtype} P={parts}")
+    case = _mk(fmt, B, ctx, 1, Hq, Hkv, D, bs, q_dtype, outlier=0.01)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.decode(num_partitions=parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle_full(case)
+    check_close(out, ref, fmt, "decode f32")
+    qt = torch.float16 if q_dtype == "f16" else torch.bfloat16
+    out16 = dc.decode(num_partitions=parts)
+    check_close(out16, ref, fmt, "decode q-dtype", out_dtype=qt)
+
+
+VERIFY_CASES = [
+    ("e5m2", 2, (8, 1000), 8, 32, 8, 128, 2048, 0),
+    ("e5m2", 3, (9, 100, 2050), 8, 32, 8, 128, 64, 3),
+    ("e4m3", 2, (70, 4096), 8, 32, 8, 128, 16, 0),
+    ("e4m3", 1, (1030,), 16, 32, 8, 128, 16, 2),
+    ("e4m3", 2, (40, 600), 3, 32, 8, 128, 16, 0),
+    ("f16", 2, (64, 300), 8, 4, 1, 64, 16, 0),
+    ("e5m2", 1, (129,), 1, 32, 8, 128, 16, 0),
+]
+
+
+@pytest.mark.parametrize("fmt,B,ctx,q_len,Hq,Hkv,D,bs,parts", VERIFY_CASES)
+def test_verify_parity(runner, fmt, B, ctx, q_len, Hq, Hkv, D, bs, parts):
+    log(f"verify {fmt} B={B} ctx={ctx} q_len={q_len} Hq={Hq} Hkv={Hkv} D={D} bs={bs} P={parts}")
+    case = _mk(fmt, B, ctx, q_len, Hq, Hkv, D, bs, "f16", sigma_kv=0.5)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.verify(q_len, num_partitions=parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle_full(case).reshape(B, q_len, Hq, D)
+    check_close(out, ref, fmt, "verify f32")
+
+
+def test_verify_rows_equal_decodes(runner):
+    """The grouped verifier is exact: row i equals a decode at ctx - q_len + 1 + i
+    (same kernels, so compared within fp32 rounding of the partition merge)."""
+    case = _mk("e5m2", 2, (300, 2100), 8, 32, 8, 128, 64, "f16", sigma_kv=0.5)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.verify(8, out_dtype=torch.float32)
+    qv = dc.q.view(2, 8, 32, 128)
+    for i in range(8):
+        ctx_i = dc.ctx_lens - 7 + i
+        od = dc.decode(q=qv[:, i].contiguous(), ctx_lens=ctx_i.contiguous(),
+                       max_ctx=int(case.ctx_lens.max()), out_dtype=torch.float32)
+        assert torch.max(torch.abs(od - out[:, i])).item() < 1e-5
+
+
+def test_decode_empty_context_rows_are_zero(runner):
+    case = _mk("e4m3", 3, (200, 300, 50), 1)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    ctx = dc.ctx_lens.clone()
+    ctx[1] = 0
+    out = dc.decode(ctx_lens=ctx, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 0).item()
+    c2 = case.ctx_lens.copy()
+    c2[1] = 0
+    from oracle import attention
+    from tests.oracle_helpers import q_f32
+    kc, vc = oracle_cache(case)
+    ref, _, _ = attention.attend(q_f32(case), [1, 1, 1], c2, kc, vc, case.block_tables, "e4m3",
+                                 case.num_kv_heads, case.softmax_scale, case.k_scale, case.v_scale)
+    check_close(out, ref, "e4m3", "decode with an empty row")
+
+
+def test_decode_is_bitwise_deterministic(runner):
+    case = _mk("e4m3", 2, (3000, 5000), 1, bs=2048)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    a = dc.decode(out_dtype=torch.float32)
+    b = dc.decode(out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_partition_count_invariance(runner):
+    case = _mk("e4m3", 1, (6000,), 1, bs=2048)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    outs = [dc.decode(num_partitions=p, out_dtype=torch.float32) for p in (1, 2, 5, 16, 94)]
+    for o in outs[1:]:
+        assert torch.max(torch.abs(o - outs[0])).item() < 2e-5
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # fmt, total, chunk, Hq, Hkv, D, bs, q_dtype
+    ("f16", 64, 64, 4, 1, 64, 16, "f16"),
+    ("e4m3", 300, 100, 32, 8, 128, 16, "bf16"),
+    ("e4m3", 1000, 333, 32, 8, 128, 2048, "bf16"),
+    ("e4m3", 700, 700, 32, 8, 128, 64, "f16"),
+    ("e5m2", 513, 257, 16, 2, 128, 32, "f16"),
+    ("e5m2", 200, 200, 8, 8, 64, 16, "bf16"),
+    ("f16", 300, 128, 8, 4, 128, 16, "f16"),
+    ("e4m3", 130, 65, 32, 1, 64, 16, "f16"),
+]
+
+
+@pytest.mark.parametrize("fmt,total,chunk,Hq,Hkv,D,bs,q_dtype", PREFILL_CASES)
+def test_prefill_chunked_parity(runner, fmt, total, chunk, Hq, Hkv, D, bs, q_dtype):
+    log(f"prefill {fmt} total={total} chunk={chunk} Hq={Hq} Hkv={Hkv} D={D} bs={bs} q={q_dtype}")
+    case = _mk(fmt, 1, (total,), total, Hq, Hkv, D, bs, q_dtype)
+    dc = runner.DeviceCase(case)
+    ref = oracle_full(case)      # unchunked: chunked == unchunked is an oracle invariant
+    outs = []
+    for s in range(0, total, chunk):
+        e = min(total, s + chunk)
+        outs.append(dc.prefill_chunk(s, e, out_dtype=torch.float32))
+    out = torch.cat(outs, 0)
+    torch.cuda.synchronize()
+    check_close(out, ref, fmt, "prefill f32")
+
+
+def test_prefill_batched_varlen(runner):
+    """Several sequences in one call, each with its own chunk length and prefix."""
+    case = _mk("e4m3", 3, (50, 400, 1200), 1, 32, 8, 128, 16, "bf16")
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    qlens = [50, 130, 257]
+    # queries: the last q_len positions of each sequence, from a fresh draw
+    rng = np.random.default_rng(5)
+    q32 = rng.standard_normal((sum(qlens), 32, 128)).astype(np.float32)
+    qb = synth.round_to(q32, "bf16")
+    from attention_paged_flashattention_amd.runner import upload16
+    qt = upload16(qb, "bf16", "cuda:0")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32, device="cuda:0")
+    out = dc.prefill(qt, cu, max(qlens), dc.ctx_lens, int(case.ctx_lens.max()),
+                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    from oracle import attention
+    kc, vc = oracle_cache(case)
+    ref, _, _ = attention.attend(synth.to_f32(qb, "bf16"), qlens, case.ctx_lens, kc, vc,
+                                 case.block_tables, "e4m3", 8, case.softmax_scale, case.k_scale,
+                                 case.v_scale)
+    check_close(out, ref, "e4m3", "prefill varlen f32")
+
+
+def test_prefill_output_dtypes(runner):
+    case = _mk("e4m3", 1, (500,), 500, 32, 8, 128, 16, "bf16")
+    dc = runner.DeviceCase(case)
+    ref = oracle_full(case)
+    dc.write_all()
+    for odt in (torch.bfloat16, torch.float16):
+        cu = torch.tensor([0, 500], dtype=torch.int32, device="cuda:0")
+        out = dc.prefill(dc.q, cu, 500, dc.ctx_lens, 500, out_dtype=odt)
+        torch.cuda.synchronize()
+        check_close(out, ref, "e4m3", f"prefill out {odt}", out_dtype=odt)
+
+
+def test_prefill_is_bitwise_deterministic(runner):
+    case = _mk("e4m3", 1, (1500,), 1500, 32, 8, 128, 2048, "bf16")
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    cu = torch.tensor([0, 1500], dtype=torch.int32, device="cuda:0")
+    a = dc.prefill(dc.q, cu, 1500, dc.ctx_lens, 1500, out_dtype=torch.float32)
+    b = dc.prefill(dc.q, cu, 1500, dc.ctx_lens, 1500, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
