@@ -4,8 +4,8 @@ Test infrastructure only (see ``oracle/__init__.py``).
 
 Paging follows "SM70 release profile and acceleration status" (KV stored in
 fixed-size token pages, 2048 tokens in the release profile, 16 as the
-``--block-size 16`` alternative) and "1Cat-vLLM 1.5.0", section "Cache, memory
-and mixed-batch reliability" (block tables hold physical page ids). The pages
+``--block-size 16`` alternative) and "1Cat-vLLM 1.5.0" RELEASE notes, section
+"Reliability and correctness fixes" (block tables hold physical page units). The pages
 do not fix a byte layout; the library's documented layout is restated here:
 
 * key cache   ``[num_blocks, num_kv_heads, block_size, head_dim]``
