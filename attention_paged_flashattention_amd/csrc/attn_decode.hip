@@ -373,6 +373,8 @@ static void launch_combine(const DecodeArgs& a, int64_t rows, int ot, hipStream_
 template <int D>
 static void launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int ot, int nqb,
                             hipStream_t stream) {
+  const ProfileEvents ev = take_profile_events();
+  record_if(ev.start, stream);
   if (fmt == KV_F16) {
     launch_split_nqb<D, KV_F16, Q_F16>(a, batch, nqb, stream);
   } else if (fmt == KV_E4M3) {
@@ -382,6 +384,7 @@ static void launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int
     if (qt == Q_BF16) launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream);
     else launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream);
   }
+  record_if(ev.stop, stream);
   const int64_t rows = (int64_t)batch * a.q_len * a.num_q_heads;
   if (fmt == KV_F16) launch_combine<D, KV_F16>(a, rows, ot, stream);
   else if (fmt == KV_E4M3) launch_combine<D, KV_E4M3>(a, rows, ot, stream);

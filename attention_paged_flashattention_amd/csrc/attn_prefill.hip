@@ -309,8 +309,11 @@ static void launch_pf_d(const PrefillArgs& a, int fmt, int qt, int ot, hipStream
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int fmt, int qt, int ot,
                           hipStream_t stream) {
   if (a.batch == 0 || a.q_blocks == 0) return hipSuccess;
+  const ProfileEvents ev = take_profile_events();
+  record_if(ev.start, stream);
   if (head_dim == 64) launch_pf_d<64>(a, fmt, qt, ot, stream);
   else launch_pf_d<128>(a, fmt, qt, ot, stream);
+  record_if(ev.stop, stream);
   return hipGetLastError();
 }
 

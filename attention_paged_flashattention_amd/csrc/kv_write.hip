@@ -76,6 +76,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const WriteArgs a) {
 
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
+  const ProfileEvents ev = take_profile_events();
+  record_if(ev.start, stream);
   dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads);
   dim3 block(256);
   if (fmt == KV_F16) {
@@ -91,6 +93,7 @@ hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStre
     else
       hipLaunchKernelGGL((kv_write_kernel<Q_F16, KV_E5M2>), grid, block, 0, stream, a);
   }
+  record_if(ev.stop, stream);
   return hipGetLastError();
 }
 

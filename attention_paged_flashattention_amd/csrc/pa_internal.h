@@ -61,6 +61,15 @@ struct PrefillArgs {
   float softmax_scale;
 };
 
+// Events to record around the next main-kernel launch on this thread (the
+// profiling hook); both null when none is pending.
+struct ProfileEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+ProfileEvents take_profile_events();
+void record_if(hipEvent_t e, hipStream_t stream);
+
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream);
 
 // fmt: KvFmt, qt: QType, ot: OType. nqb: number of 16-row query blocks.

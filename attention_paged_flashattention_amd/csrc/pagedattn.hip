@@ -25,6 +25,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local pa::ProfileEvents g_profile;
 
 pa_status fail(pa_status st, const char* fmt, ...) {
   char buf[512];
@@ -211,7 +212,27 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
 
 }  // namespace
 
+namespace pa {
+ProfileEvents take_profile_events() {
+  ProfileEvents e = g_profile;
+  g_profile = ProfileEvents{};
+  return e;
+}
+void record_if(hipEvent_t e, hipStream_t stream) {
+  if (e) (void)hipEventRecord(e, stream);
+}
+}  // namespace pa
+
 extern "C" {
+
+PA_API void pa_profile_next_call(void* start_event, void* stop_event) {
+  if (!start_event || !stop_event) {
+    g_profile = pa::ProfileEvents{};
+    return;
+  }
+  g_profile.start = static_cast<hipEvent_t>(start_event);
+  g_profile.stop = static_cast<hipEvent_t>(stop_event);
+}
 
 PA_API const char* pa_last_error(void) { return g_last_error.c_str(); }
 

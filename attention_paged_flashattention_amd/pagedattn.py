@@ -26,7 +26,8 @@ TORCH_DTYPES = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float32: P
 
 EXPORTS = ["kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
            "attn_verify_paged", "pa_decode_partitions", "pa_workspace_bytes",
-           "pa_supports", "pa_last_error", "pa_version", "pa_validate_tables"]
+           "pa_supports", "pa_last_error", "pa_version", "pa_validate_tables",
+           "pa_profile_next_call"]
 
 
 class PagedAttnError(RuntimeError):
@@ -62,6 +63,8 @@ _lib.pa_supports.restype = _i32
 _lib.pa_last_error.restype = ctypes.c_char_p
 _lib.pa_version.restype = ctypes.c_char_p
 _lib.pa_validate_tables.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i64, _vp]
+_lib.pa_profile_next_call.argtypes = [_vp, _vp]
+_lib.pa_profile_next_call.restype = None
 for _name in ("kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
               "attn_verify_paged", "pa_validate_tables"):
     getattr(_lib, _name).restype = _i32
@@ -216,6 +219,12 @@ def attn_verify_paged(q, key_cache, value_cache, cache_dtype, block_tables, cont
                         value_cache, cache_dtype, block_tables, context_lens, max_context_len,
                         softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
                         out_dtype, stream)
+
+
+def pa_profile_next_call(start_event, stop_event):
+    """Record the two hipEvent_t handles (ints) around the main kernel of the
+    next call on this thread."""
+    _lib.pa_profile_next_call(ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event))
 
 
 def pa_validate_tables(block_tables, context_lens, max_context_len, block_size, num_blocks,

@@ -1,0 +1,403 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections ...]
+
+Prints ONE JSON line. ``value`` is the headline: decode at 128K context over
+an FP8 E4M3 block-paged cache (1 sequence, 32 query / 8 KV heads, head_dim 128,
+2048-token pages, 64 split-KV partitions), in GB/s of algorithmic bytes. One
+step = quantize-on-write of the newest token, the split-KV kernel and the
+log-sum-exp combine -- every step of the decode path. Four copies of the 256 MiB
+cache are used in rotation so that no step finds its cache in the 256 MB
+last-level cache. The same line carries the 32K chunked-prefill throughput
+(useful causal TFLOP/s; one step = 8 chunks of 4096 tokens, each a write then a
+prefill), the q8 verify at 128K, the 256K decode and the batched decode, the
+roofline of the dominant kernels (timed with HIP events recorded by the
+library around the kernel, on its stream), and the CPU oracle timed on a
+bounded sample of the headline workload.
+
+Inputs are synthetic and seeded (attention_paged_flashattention_amd.synth) and
+already resident in HBM when a timed region starts.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS_16 = 2500.0    # MI355X dense fp16 / bf16 MFMA
+METRIC = "paged-attn decode GB/s (%HBM peak) @128K FP8 KV; prefill TFLOP/s @32K"
+SECTIONS = ["decode128k", "prefill32k", "verify128k", "decode256k", "decode_b8", "copy"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime first)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "attention_paged_flashattention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters(name, kernel_sha):
+    """HBM traffic per launch from the committed rocprofv3 --pmc summary, or
+    None when absent or taken on a different version of the kernel."""
+    path = os.path.join(ROOT, "profiles", f"{name}.counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_sha:
+        return None
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i, True)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
+    """Write the newest q_len tokens of every sequence, then decode/verify.
+    Returns a result dict with the step time and the split kernel's times."""
+    import torch
+    from attention_paged_flashattention_amd import pagedattn as pa
+    from attention_paged_flashattention_amd import runner
+
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    kcs = [dc.key_cache] + [dc.key_cache.clone() for _ in range(copies - 1)]
+    vcs = [dc.value_cache] + [dc.value_cache.clone() for _ in range(copies - 1)]
+    newest = dc.last_token_rows(q_len)
+    k_new, v_new, s_new = dc.k[newest].contiguous(), dc.v[newest].contiguous(), dc.slots[newest].contiguous()
+    c = case
+    parts = c.meta.get("partitions", 0)
+    op = pa.PA_OP_DECODE if q_len == 1 else pa.PA_OP_VERIFY
+    wsb = pa.pa_workspace_bytes(op, c.batch, q_len, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                parts, dc.max_ctx)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dc.device)
+    qv = dc.q if q_len == 1 else dc.q.view(c.batch, q_len, c.num_q_heads, c.head_dim)
+    out = torch.empty_like(qv)
+    starts = [ev.create() for _ in range(steps)]
+    stops = [ev.create() for _ in range(steps)]
+    fn_call = pa.attn_decode_paged if q_len == 1 else pa.attn_verify_paged
+    torch.cuda.synchronize()
+
+    def step(i, record):
+        kc, vc = kcs[i % copies], vcs[i % copies]
+        pa.kv_cache_write_fp8(k_new, v_new, s_new, kc, vc, c.cache_fmt, dc.k_scale, dc.v_scale)
+        if record:
+            pa.pa_profile_next_call(starts[i], stops[i])
+        fn_call(qv, kc, vc, c.cache_fmt, dc.block_tables, dc.ctx_lens, dc.max_ctx,
+                c.softmax_scale, dc.k_scale, dc.v_scale, num_partitions=parts, workspace=ws,
+                out=out)
+
+    ms = timed(step, steps, warmup)
+    kern = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+    kv_bytes = int(sum(int(x) for x in c.ctx_lens)) * c.num_kv_heads * c.head_dim * 2 * \
+        (1 if c.cache_fmt != "f16" else 2)
+    rows = c.batch * q_len * c.num_q_heads
+    qo = rows * c.head_dim * 2
+    meta = sum(-(-int(x) // c.block_size) for x in c.ctx_lens) * 4 + \
+        (0 if c.k_scale is None else 2 * c.num_kv_heads * 4)
+    newest_n = len(newest)
+    write_bytes = newest_n * c.num_kv_heads * c.head_dim * (2 * 2 + 2) + newest_n * 8
+    step_bytes = kv_bytes + meta + 2 * qo + write_bytes
+    split_bytes = kv_bytes + meta + qo
+    kern_ms = sum(kern) / len(kern)
+    del kcs, vcs, dc
+    torch.cuda.empty_cache()
+    return dict(name=name, ms_per_step=ms, step_bytes=step_bytes, GBps=step_bytes / ms / 1e6,
+                split_ms=kern_ms, split_bytes=split_bytes,
+                split_GBps=split_bytes / kern_ms / 1e6,
+                partitions=pa.pa_decode_partitions(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
+                                                   c.head_dim, dc_max(c)) if parts == 0 else parts)
+
+
+def dc_max(c):
+    return int(max(int(x) for x in c.ctx_lens))
+
+
+def prefill_section(ev, steps, warmup):
+    import torch
+    from attention_paged_flashattention_amd import pagedattn as pa
+    from attention_paged_flashattention_amd import runner, synth
+
+    case = synth.chunked_prefill_32k()
+    dc = runner.DeviceCase(case)
+    chunk = case.meta["chunk"]
+    n = 32768 // chunk
+    dev = dc.device
+    cu = torch.tensor([0, chunk], dtype=torch.int32, device=dev)
+    ctxs = [torch.tensor([chunk * (i + 1)], dtype=torch.int32, device=dev) for i in range(n)]
+    out = torch.empty((chunk, case.num_q_heads, case.head_dim), dtype=dc.q.dtype, device=dev)
+    starts = [[ev.create() for _ in range(n)] for _ in range(steps)]
+    stops = [[ev.create() for _ in range(n)] for _ in range(steps)]
+    torch.cuda.synchronize()
+
+    def step(i, record):
+        for ci in range(n):
+            s, e = ci * chunk, (ci + 1) * chunk
+            pa.kv_cache_write_fp8(dc.k[s:e], dc.v[s:e], dc.slots[s:e], dc.key_cache,
+                                  dc.value_cache, case.cache_fmt, dc.k_scale, dc.v_scale)
+            if record:
+                pa.pa_profile_next_call(starts[i][ci], stops[i][ci])
+            pa.attn_prefill_paged(dc.q[s:e], cu, chunk, dc.key_cache, dc.value_cache,
+                                  case.cache_fmt, dc.block_tables, ctxs[ci], e, case.softmax_scale,
+                                  dc.k_scale, dc.v_scale, out=out)
+
+    ms = timed(step, steps, warmup)
+    per_chunk = [[ev.elapsed_ms(a, b) for a, b in zip(sa, so)] for sa, so in zip(starts, stops)]
+    D, Hq = case.head_dim, case.num_q_heads
+    chunk_flops = [4 * D * Hq * (chunk * chunk * ci + chunk * (chunk + 1) // 2) for ci in range(n)]
+    flops = sum(chunk_flops)
+    kern_ms = sum(sum(x) for x in per_chunk) / steps
+    last_ms = sum(x[-1] for x in per_chunk) / steps
+    del dc
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms, flops=flops, TFLOPs=flops / ms / 1e9,
+                kernel_ms=kern_ms, kernel_TFLOPs=flops / kern_ms / 1e9,
+                last_chunk_ms=last_ms, last_chunk_TFLOPs=chunk_flops[-1] / last_ms / 1e9,
+                launches_per_step=n)
+
+
+def copy_section(ev, steps):
+    """Achievable HBM bandwidth of a plain device copy (context, and the
+    calibration kernel for the traffic counters)."""
+    import torch
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes=2 * nbytes, ms=ms, GBps=2 * nbytes / ms / 1e6)
+
+
+def cpu_baseline(seconds_target=10.0):
+    """The oracle, as it stands, on a bounded sample of the 128K decode step:
+    2 of the 8 KV heads (8 of 32 query heads) over the full context. The
+    oracle's cache for those heads is built untimed (the cache is resident on
+    the GPU side too); timed: the oracle's write of the newest token and its
+    attention for the 8 sampled query heads, repeated to ~10 s."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(seconds_target)
+
+
+def _cpu_baseline(seconds_target):
+    from attention_paged_flashattention_amd import synth
+    from oracle import attention, paged
+
+    case = synth.headline_decode_128k()
+    heads_kv = [0, 5]
+    fill = synth.POISON["e4m3"]
+    kc, vc = paged.new_caches(case.num_blocks, case.num_kv_heads, case.block_size,
+                              case.head_dim, "e4m3", fill=fill)
+    ctx = int(case.ctx_lens[0])
+    slots = case.slot_mapping
+    bs = case.block_size
+    k32 = synth.to_f32(case.k, "f16")
+    v32 = synth.to_f32(case.v, "f16")
+    for g in heads_kv:
+        page, off = slots[:ctx - 1] // bs, slots[:ctx - 1] % bs
+        kc[page, g, off, :] = paged.quantize(k32[:ctx - 1, g, :], "e4m3", case.k_scale[g])
+        vc[page, g, :, off] = paged.quantize(v32[:ctx - 1, g, :], "e4m3", case.v_scale[g])
+    q32 = synth.to_f32(case.q, "f16")
+    G = case.gqa
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for g in heads_kv:
+            t = ctx - 1
+            page, off = slots[t] // bs, slots[t] % bs
+            kc[page, g, off, :] = paged.quantize(k32[t, g, :], "e4m3", case.k_scale[g])
+            vc[page, g, :, off] = paged.quantize(v32[t, g, :], "e4m3", case.v_scale[g])
+            heads = [g * G + i for i in range(G)]
+            attention.attend_rows(q32[0, heads], heads, [ctx - 1] * G, ctx, kc, vc,
+                                  case.block_tables[0], "e4m3", case.num_q_heads,
+                                  case.num_kv_heads, case.softmax_scale, case.k_scale,
+                                  case.v_scale)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds_target:
+            break
+    dt = time.perf_counter() - t0
+    sample_bytes = len(heads_kv) * ctx * case.head_dim * 2 * reps
+    return dict(value=sample_bytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=(f"2 of 8 KV heads (8 of 32 query heads) of the 128K E4M3 decode step, "
+                        f"full 131072-token context, {reps} repetitions in {dt:.1f} s; numpy "
+                        f"float64, BLAS limited to 1 thread; host has {os.cpu_count()} CPUs"),
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma-separated subset of " + ",".join(SECTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    ws = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or ws != 1:
+        print("bench.py: this build runs on exactly one GPU (no sharding, no collectives); "
+              f"--gpus {args.gpus} / WORLD_SIZE {ws} is not supported", file=sys.stderr)
+        sys.exit(2)
+    sections = [s for s in args.sections.split(",") if s]
+    for s in sections:
+        if s not in SECTIONS:
+            ap.error(f"unknown section {s}")
+
+    import torch
+    from attention_paged_flashattention_amd import build as build_mod
+    if not os.path.exists(build_mod.OUT):
+        build_mod.build()
+    from attention_paged_flashattention_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    res = {}
+
+    if "copy" in sections:
+        log("section copy")
+        res["copy"] = copy_section(ev, max(5, K // 2))
+    if "decode128k" in sections:
+        log("section decode128k")
+        res["decode128k"] = decode_like_section(ev, synth.headline_decode_128k(), K, W, 4, 1,
+                                                "decode_128k_e4m3_bs2048_p64")
+    if "prefill32k" in sections:
+        log("section prefill32k")
+        res["prefill32k"] = prefill_section(ev, max(2, K // 5), max(1, W // 5))
+    if "verify128k" in sections:
+        log("section verify128k")
+        res["verify128k"] = decode_like_section(ev, synth.verify_q8_128k(), K, W, 1, 8,
+                                                "verify_q8_b4_128k_e5m2_bs2048")
+    if "decode256k" in sections:
+        log("section decode256k")
+        res["decode256k"] = decode_like_section(ev, synth.long_decode_256k(), K, W, 1, 1,
+                                                "decode_256k_e4m3_bs2048_p64")
+    if "decode_b8" in sections:
+        log("section decode_b8")
+        res["decode_b8"] = decode_like_section(ev, synth.batched_decode_e4m3(), K, W, 8, 1,
+                                               "decode_b8_1k4k_e4m3_bs16")
+
+    cpu = None
+    if not args.no_cpu_baseline and "decode128k" in sections:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+
+    dec_sha = source_hash("attn_decode.hip", "pa_device.h")
+    pf_sha = source_hash("attn_prefill.hip", "pa_device.h")
+    line = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": W, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    h = res.get("decode128k")
+    if h:
+        line.update(value=round(h["GBps"], 1), unit="GB/s", ms_per_step=round(h["ms_per_step"], 5))
+        line["dtype"] = "fp16"
+        line["config"] = {"workload": h["name"], "batch": 1, "context": 131072,
+                          "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                          "block_size": 2048, "kv_cache": "fp8_e4m3 per-head scales",
+                          "partitions": h["partitions"], "cache_copies_rotated": 4}
+        ach = h["split_GBps"]
+        tr = counters("decode_split_128k_e4m3", dec_sha)
+        line["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel",
+                            "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": tr,
+                            "algorithmic_bytes_per_launch": h["split_bytes"],
+                            "avg_launch_us": round(h["split_ms"] * 1e3, 2)}
+    else:
+        line.update(value=None, unit="GB/s", ms_per_step=None, dtype="fp16", config={})
+    p = res.get("prefill32k")
+    if p:
+        line["prefill_32k"] = {"workload": "prefill32k_chunk4k_bf16_e4m3_bs2048",
+                               "TFLOPs": round(p["TFLOPs"], 1), "ms_per_step": round(p["ms_per_step"], 3),
+                               "frac_of_peak": round(p["TFLOPs"] / MFMA_PEAK_TFLOPS_16, 4),
+                               "useful_causal_flops": p["flops"],
+                               "last_chunk_TFLOPs": round(p["last_chunk_TFLOPs"], 1),
+                               "last_chunk_ms": round(p["last_chunk_ms"], 3), "dtype": "bf16"}
+        trp = counters("prefill_32k_e4m3", pf_sha)
+        line["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel",
+                                    "achieved": round(p["kernel_TFLOPs"], 1),
+                                    "peak": MFMA_PEAK_TFLOPS_16, "unit": "TFLOP/s",
+                                    "frac": round(p["kernel_TFLOPs"] / MFMA_PEAK_TFLOPS_16, 4),
+                                    "traffic": trp,
+                                    "algorithmic_flops_per_step": p["flops"],
+                                    "avg_launch_us": round(p["kernel_ms"] / p["launches_per_step"] * 1e3, 1)}
+    for key, out_key in [("verify128k", "verify_q8_128k"), ("decode256k", "decode_256k"),
+                         ("decode_b8", "decode_b8")]:
+        r = res.get(key)
+        if r:
+            line[out_key] = {"workload": r["name"], "GBps": round(r["GBps"], 1),
+                             "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                             "frac_of_hbm_peak": round(r["GBps"] / HBM_PEAK_GBPS, 4),
+                             "split_kernel_GBps": round(r["split_GBps"], 1),
+                             "split_kernel_us": round(r["split_ms"] * 1e3, 2),
+                             "partitions": r["partitions"]}
+    if "copy" in res:
+        line["hbm_copy_GBps"] = round(res["copy"]["GBps"], 1)
+    if cpu:
+        line["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                for k, v in cpu.items() if k != "seconds"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -214,6 +214,17 @@ PA_API const char* pa_last_error(void);
 PA_API const char* pa_version(void);
 
 /*
+ * Profiling hook (in the spirit of the pages' per-route performance counters,
+ * "SM70 release profile and acceleration status"): start_event and stop_event
+ * are hipEvent_t handles owned by the caller. The next write or attention call
+ * made on the calling thread records start_event on its stream immediately
+ * before its main kernel (the write kernel, the prefill kernel, or the split
+ * kernel of decode/verify) and stop_event immediately after it, then forgets
+ * both. Passing NULL for either clears a pending request. No effect on results.
+ */
+PA_API void pa_profile_next_call(void* start_event, void* stop_event);
+
+/*
  * Debug check, synchronous, never on the hot path: copies context_lens and
  * block_tables to the host (after synchronizing `stream`) and verifies
  * 0 <= context_lens[b] <= min(max_context_len, max_blocks_per_seq *
