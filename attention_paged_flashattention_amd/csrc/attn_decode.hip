@@ -19,9 +19,10 @@
 //   reads it. Keys are dealt to MFMA rows so that each lane's S^T outputs are
 //   exactly the 16 keys it later feeds as the B operand of O^T += V^T P^T --
 //   P never moves between lanes.
-// * Values are stored dimension-major in each page, so a lane's 16 keys of one
-//   head dimension are 16 contiguous bytes: the A operand of the PV MFMA is one
-//   128-bit load, no transpose.
+// * Values are stored dimension-major inside 64-token groups of a page, so a
+//   lane's 16 keys of one head dimension are 16 contiguous bytes (the A operand
+//   of the PV MFMA is one 128-bit load, no transpose) and a tile's values are
+//   one contiguous 8 KiB run, like its keys.
 // * Online softmax per row in exp2 units; the row max is reduced across the 4
 //   lanes that share a row with two cross-lane exchanges, the row sum stays
 //   lane-partial until the end.
@@ -73,14 +74,46 @@ __device__ __forceinline__ half8 val_op(const uint32_t* dw) {
 
 constexpr float kNegInf = -__builtin_inff();
 
-template <int D, int FMT, int QT, int NQB>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
+// Raw cache bytes of one 64-key tile as one lane holds them.
+template <int D, int ES>
+struct DecodeTile {
+  static constexpr int KDW = (D / 4) * ES / 4;  // dwords per lane per key row run
+  static constexpr int DB = D / 16;             // 16-dim blocks
+  static constexpr int VDW = 16 * ES / 4;       // dwords per lane per 16-key value run
+  uint32_t k[4][KDW];
+  uint32_t v[DB][VDW];
+};
+
+// Physical pages of the two 16-key runs a lane touches in a tile (its K run
+// and its V run). With pages of >= 64 keys both are the tile's one page.
+struct TilePages {
+  int64_t k, v;
+};
+
+__device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// UNI: block_size >= 64, so every 64-key tile lies in one page and its page id
+// is wave-uniform (a scalar load).
+// PIPE: two register stages (the next tile's loads in flight while this one is
+// multiplied); used where both stages fit in the registers of 2 waves per SIMD
+// (FP8 cache, one 16-row query block). Otherwise tiles are loaded one at a time
+// and the waves of the CU overlap each other's loads.
+template <int FMT, int NQB>
+struct DecodePipe {
+  static constexpr bool value = FMT != KV_F16 && NQB == 1;
+};
+
+template <int D, int FMT, int QT, int NQB, bool UNI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodePipe<FMT, NQB>::value ? 2 : 1)))
+void decode_split_kernel(const DecodeArgs a) {
+  constexpr bool PIPE = DecodePipe<FMT, NQB>::value;
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;  // bytes per cache element
   constexpr int KSTEPS = D / 32;               // MFMA k-steps over the head dim
   constexpr int RUN = D / 4;                   // key elements per lane per key row
-  constexpr int KDW = RUN * ES / 4;            // dwords per lane per key row
-  constexpr int DB = D / 16;                   // 16-dim blocks of the output
-  constexpr int VDW = 16 * ES / 4;             // dwords per lane per value run
+  using Tile = DecodeTile<D, ES>;
+  constexpr int KDW = Tile::KDW, DB = Tile::DB, VDW = Tile::VDW;
   using OpT = typename QOp<QT>::T;
 
   __shared__ float sm_o[4][D][17];
@@ -88,7 +121,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   __shared__ float sm_l[4][16];
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15;   // MFMA column: query row within a 16-row block
   const int qg = lane >> 4;  // MFMA k-group
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -97,9 +131,76 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   const int tb = p * a.part_len;
   const int te = min(tb + a.part_len, ctx);
   const int ntiles = te > tb ? (te - tb + 63) >> 6 : 0;
+  const int J = ntiles > w ? (ntiles - w + 3) >> 2 : 0;  // tiles of this wave: w + 4 j
   const int bs_log2 = a.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
+  const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
+  const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
+  const int64_t kv_heads = a.num_kv_heads;
+  const int first_masked = ctx - a.q_len + 1;  // smallest key some row cannot see
+
+  auto tile_t0 = [&](int j) { return tb + ((w + 4 * j) << 6); };
+  auto need_mask = [&](int t0) { return t0 + 64 > first_masked; };
+
+  // Page ids of tile j (loaded one tile before they are used).
+  auto pages = [&](int j) {
+    TilePages pg;
+    const int t0 = tile_t0(j);
+    if constexpr (UNI) {
+      pg.k = pg.v = btb[t0 >> bs_log2];
+    } else {
+      const int tk = t0 + 16 * (c >> 2), tv = t0 + 16 * qg;
+      pg.k = tk < ctx ? btb[tk >> bs_log2] : 0;
+      pg.v = tv < ctx ? btb[tv >> bs_log2] : 0;
+    }
+    return pg;
+  };
+
+  // Issue the 128-bit streaming loads of tile j, unconditionally: a run past
+  // the context still reads a valid page (its own page, or page 0 for a run
+  // whose page is beyond the block table), and compute() masks those keys by
+  // select -- S to -inf, V to zero -- whatever the stale slot holds. Keeping
+  // the loads unconditional lets the compiler count them exactly, so one
+  // tile's loads stay in flight while another is multiplied.
+  auto load = [&](Tile& T, int j, const TilePages& pg) {
+    const int t0 = tile_t0(j);
+    const int tk = t0 + 16 * (c >> 2);  // first key of this lane's K run
+    const int tv = t0 + 16 * qg;        // first key of this lane's V run
+    const uint8_t* kp = a.key_cache +
+        (((pg.k * kv_heads + g) << bs_log2) + (tk & bs_mask) + (c & 3)) * (int64_t)(D * ES) +
+        RUN * qg * ES;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int x = 0; x < KDW / 4; ++x) {
+        u32x4 v = ld16_stream(kp + (int64_t)4 * s * D * ES + 16 * x);
+        T.k[s][4 * x] = v.x; T.k[s][4 * x + 1] = v.y;
+        T.k[s][4 * x + 2] = v.z; T.k[s][4 * x + 3] = v.w;
+      }
+    // values: dimension-major inside groups of 2^vg_log2 tokens of a page
+    const int vo = tv & bs_mask;
+    const uint8_t* vp = a.value_cache +
+        (((((pg.v * kv_heads + g) << (bs_log2 - vg_log2)) + (vo >> vg_log2)) * D + c) << vg_log2 |
+         (vo & ((1 << vg_log2) - 1))) * (int64_t)ES;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int x = 0; x < VDW / 4; ++x) {
+        u32x4 v = ld16_stream(vp + ((int64_t)(db * 16) << vg_log2) * ES + 16 * x);
+        T.v[db][4 * x] = v.x; T.v[db][4 * x + 1] = v.y;
+        T.v[db][4 * x + 2] = v.z; T.v[db][4 * x + 3] = v.w;
+      }
+  };
+
   const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
+
+  // Start the first tile's traffic before anything else.
+  Tile A, B;
+  TilePages P0{0, 0}, P1{0, 0};
+  if (J > 0) P0 = pages(0);
+  if (J > 1) P1 = pages(1);
+  if (J > 0) load(A, 0, P0);
+  (void)B;
 
   // Query operands (B of S^T = K Q^T): row r = nb*16 + c, head dims
   // RUN*qg + 8j .. +7 for k-step j. Padding rows are zero.
@@ -128,80 +229,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
     for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{0, 0, 0, 0};
   }
 
-  const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
-  const int64_t kv_heads = a.num_kv_heads;
-  const int first_masked = ctx - a.q_len + 1;  // smallest key some row cannot see
-
-  for (int n = w; n < ntiles; n += 4) {
-    const int t0 = tb + (n << 6);
-    const bool need_mask = t0 + 64 > first_masked;
-    const int tk = t0 + 16 * (c >> 2);  // first key of this lane's K group
-    const int tv = t0 + 16 * qg;        // first key of this lane's V group
-    const bool kok = !need_mask || tk < ctx;
-    const bool vok = !need_mask || tv < ctx;
-
-    uint32_t kraw[4][KDW];
-    uint32_t vraw[DB][VDW];
-    if (kok) {
-      const int64_t page = btb[tk >> bs_log2];
-      const uint8_t* kp = a.key_cache +
-          (((page * kv_heads + g) << bs_log2) + (tk & bs_mask) + (c & 3)) * (int64_t)(D * ES) +
-          RUN * qg * ES;
+  auto compute = [&](Tile& T, int j) {
+    const int t0 = tile_t0(j);
+    const bool nm = need_mask(t0);
+    if (nm) {
+      const int tv = t0 + 16 * qg;
+      const int nvalid = ctx - tv;
+      if (nvalid < 16) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+        for (int e = 0; e < 16; ++e) {
+          if (e >= nvalid) {
 #pragma unroll
-        for (int x = 0; x < KDW / 4; ++x) {
-          u32x4 v = ld16(kp + (int64_t)4 * s * D * ES + 16 * x);
-          kraw[s][4 * x] = v.x; kraw[s][4 * x + 1] = v.y;
-          kraw[s][4 * x + 2] = v.z; kraw[s][4 * x + 3] = v.w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int x = 0; x < KDW; ++x) kraw[s][x] = 0;
-    }
-    if (vok) {
-      const int64_t page = btb[tv >> bs_log2];
-      const uint8_t* vp = a.value_cache +
-          ((((page * kv_heads + g) * D + c) << bs_log2) + (tv & bs_mask)) * (int64_t)ES;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int x = 0; x < VDW / 4; ++x) {
-          u32x4 v = ld16(vp + ((int64_t)(db * 16) << bs_log2) * ES + 16 * x);
-          vraw[db][4 * x] = v.x; vraw[db][4 * x + 1] = v.y;
-          vraw[db][4 * x + 2] = v.z; vraw[db][4 * x + 3] = v.w;
-        }
-      }
-      if (need_mask) {
-        // zero the value elements of keys past the context (select, never
-        // multiply: a poisoned slot may hold NaN)
-        const int nvalid = ctx - tv;  // >= 1 here
-        if (nvalid < 16) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            if (e >= nvalid) {
-#pragma unroll
-              for (int db = 0; db < DB; ++db) {
-                if constexpr (ES == 1) {
-                  vraw[db][e >> 2] &= ~(0xFFu << ((e & 3) * 8));
-                } else {
-                  vraw[db][e >> 1] &= ~(0xFFFFu << ((e & 1) * 16));
-                }
-              }
+            for (int db = 0; db < DB; ++db) {
+              if constexpr (ES == 1) T.v[db][e >> 2] &= ~(0xFFu << ((e & 3) * 8));
+              else T.v[db][e >> 1] &= ~(0xFFFFu << ((e & 1) * 16));
             }
           }
         }
       }
-    } else {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int x = 0; x < VDW; ++x) vraw[db][x] = 0;
     }
-
     // S^T = K Q^T: S-tile s row i of k-group qg holds key t0 + 16 qg + 4 s + i.
     f32x4 sacc[NQB][4];
 #pragma unroll
@@ -211,14 +257,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        OpT kop = key_op<FMT, QT>(&kraw[s][j * (8 * ES / 4)]);
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        OpT kop = key_op<FMT, QT>(&T.k[s][kk * (8 * ES / 4)]);
 #pragma unroll
-        for (int nb = 0; nb < NQB; ++nb) sacc[nb][s] = mfma_qk<QT>(kop, qop[nb][j], sacc[nb][s]);
+        for (int nb = 0; nb < NQB; ++nb) sacc[nb][s] = mfma_qk<QT>(kop, qop[nb][kk], sacc[nb][s]);
       }
     }
-
-    if (need_mask) {
+    if (nm) {
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
         const int r = nb * 16 + c;
@@ -230,7 +275,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
             if (t0 + 16 * qg + 4 * s + i > lim) sacc[nb][s][i] = kNegInf;
       }
     }
-
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
       float tm = kNegInf;
@@ -261,10 +305,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
         o[nb][db] *= alpha;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          half8 vop = val_op<FMT>(&vraw[db][hh * (8 * ES / 4)]);
+          half8 vop = val_op<FMT>(&T.v[db][hh * (8 * ES / 4)]);
           o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[hh], o[nb][db], 0, 0, 0);
         }
       }
+    }
+  };
+
+  if constexpr (PIPE) {
+    // Two-stage pipeline: tile j+1's loads are in flight while tile j is
+    // multiplied; page ids run one more tile ahead. The loop body issues its
+    // loads unconditionally; the last one or two tiles are peeled.
+    int j = 0;
+    for (; j + 2 < J; j += 2) {
+      P0 = pages(j + 2);
+      load(B, j + 1, P1);
+      compute(A, j);
+      if (j + 3 < J) P1 = pages(j + 3);
+      load(A, j + 2, P0);
+      compute(B, j + 1);
+    }
+    if (j + 1 < J) {
+      load(B, j + 1, P1);
+      compute(A, j);
+      compute(B, j + 1);
+    } else if (j < J) {
+      compute(A, j);
+    }
+  } else {
+    // One stage; page ids one tile ahead.
+    for (int j = 0; j < J; ++j) {
+      if (j > 0) load(A, j, P1);
+      if (j + 1 < J) P1 = pages(j + 1);
+      compute(A, j);
     }
   }
 
@@ -313,46 +386,89 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
   }
 }
 
-// One wave per output row: out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p,
-// partitions in index order, empty ones (m_p = -inf) left out; times the
-// per-head value scale. A row with no visible key is written as zeros.
+// One work-group of 256 threads per output row:
+//   out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
+// over the partitions in index order; empty partitions (m_p = -inf) weigh 0.
+// Times the per-head value scale. A row with no visible key is written as zeros.
+// The partition weights are computed once into LDS; each thread then sums a
+// fixed slice of partitions for one head dimension, and the slices are added
+// in a fixed order, so the result does not depend on timing.
+constexpr int kCombineThreads = 256;
+constexpr int kMaxCombineParts = 4096;
+
 template <int D, int FMT, int OT>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeArgs a) {
-  constexpr int PER = D / 64;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeArgs a) {
+  constexpr int SL = kCombineThreads / D;  // partition slices (2 at D = 128, 4 at D = 64)
+  __shared__ float sw[kMaxCombineParts];
+  __shared__ float sred[kCombineThreads];
+  __shared__ float sacc[SL][D];
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int h = (int)(row % a.num_q_heads);
   const int g = h / G;
   const int P = a.num_parts;
   const float* ml = a.ws_ml + row * P * 2;
   const float* po = a.ws_o + row * P * D;
+
   float M = kNegInf;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, ml[2 * p]);
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-  float L = 0.0f;
-  if (M != kNegInf) {
-    for (int p = 0; p < P; ++p) {
-      const float mp = ml[2 * p];
-      if (mp == kNegInf) continue;
-      const float wt = __builtin_amdgcn_exp2f(mp - M);
-      L += wt * ml[2 * p + 1];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += wt * po[(int64_t)p * D + lane + 64 * k];
-    }
+  for (int p = t; p < P; p += kCombineThreads) M = fmaxf(M, ml[2 * p]);
+  sred[t] = M;
+  __syncthreads();
+  for (int s = kCombineThreads / 2; s > 0; s >>= 1) {
+    if (t < s) sred[t] = fmaxf(sred[t], sred[t + s]);
+    __syncthreads();
   }
-  const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
-  const float f = L > 0.0f ? vscale / L : 0.0f;
+  M = sred[0];
+  __syncthreads();
+  float lsum = 0.0f;
+  for (int p = t; p < P; p += kCombineThreads) {
+    const float mp = ml[2 * p];
+    const float wt = (mp == kNegInf || M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
+    sw[p] = wt;
+    lsum += wt * ml[2 * p + 1];
+  }
+  sred[t] = lsum;
+  __syncthreads();
+  for (int s = kCombineThreads / 2; s > 0; s >>= 1) {
+    if (t < s) sred[t] += sred[t + s];
+    __syncthreads();
+  }
+  const float L = sred[0];
+
+  const int d = t % D, sl = t / D;
+  const int per = (P + SL - 1) / SL;
+  const int p0 = sl * per, p1 = min(P, p0 + per);
+  float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+  int p = p0;
+  for (; p + 4 <= p1; p += 4) {
+    const float o0 = po[(int64_t)p * D + d], o1 = po[(int64_t)(p + 1) * D + d];
+    const float o2 = po[(int64_t)(p + 2) * D + d], o3 = po[(int64_t)(p + 3) * D + d];
+    acc0 += sw[p] * o0;
+    acc1 += sw[p + 1] * o1;
+    acc2 += sw[p + 2] * o2;
+    acc3 += sw[p + 3] * o3;
+  }
+  for (; p < p1; ++p) acc0 += sw[p] * po[(int64_t)p * D + d];
+  sacc[sl][d] = (acc0 + acc1) + (acc2 + acc3);
+  __syncthreads();
+  if (sl == 0) {
+    float acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) store_out<OT>(a.out, row * D + lane + 64 * k, acc[k] * f);
+    for (int k = 0; k < SL; ++k) acc += sacc[k][d];
+    const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
+    const float f = L > 0.0f ? vscale / L : 0.0f;
+    store_out<OT>(a.out, row * D + d, acc * f);
+  }
 }
 
 template <int D, int FMT, int QT, int NQB>
 static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
   dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB>), grid, dim3(256), 0, stream, a);
+  if (a.bs_log2 >= 6)
+    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, false>), grid, dim3(256), 0, stream, a);
 }
 
 template <int D, int FMT, int QT>
@@ -364,7 +480,7 @@ static void launch_split_nqb(const DecodeArgs& a, int batch, int nqb, hipStream_
 
 template <int D, int FMT>
 static void launch_combine(const DecodeArgs& a, int64_t rows, int ot, hipStream_t stream) {
-  dim3 grid((unsigned)rows), block(64);
+  dim3 grid((unsigned)rows), block(kCombineThreads);
   if (ot == O_F32) hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_F32>), grid, block, 0, stream, a);
   else if (ot == O_F16) hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_F16>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_BF16>), grid, block, 0, stream, a);

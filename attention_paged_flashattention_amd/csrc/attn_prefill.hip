@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int c32 = lane & 31, hgrp = lane >> 5;
   const int bs_log2 = a.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
+  const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
   const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
   const int64_t kvh = Hkv;
 
@@ -139,8 +140,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       const int k0 = t0 + vk0 + x * KPL;
       if (k0 < ctx) {
         const int64_t page = btb[k0 >> bs_log2];
+        const int vo = k0 & bs_mask;  // values: dimension-major inside 2^vg_log2-token groups
         const uint8_t* vp = a.value_cache +
-            ((((page * kvh + g) * D + vd) << bs_log2) + (k0 & bs_mask)) * (int64_t)ES;
+            (((((page * kvh + g) << (bs_log2 - vg_log2)) + (vo >> vg_log2)) * D + vd) << vg_log2 |
+             (vo & ((1 << vg_log2) - 1))) * (int64_t)ES;
         u32x4 v = ld16(vp);
         const int nvalid = ctx - k0;
         if (nvalid < KPL) {

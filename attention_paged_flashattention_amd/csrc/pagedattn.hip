@@ -18,7 +18,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/pagedattn.h"
+#include "pagedattn.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 

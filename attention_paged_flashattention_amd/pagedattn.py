@@ -113,21 +113,48 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims")
 
 
-def kv_cache_write_fp8(key, value, slot_mapping, key_cache, value_cache, cache_dtype,
-                       k_scale=None, v_scale=None, stream=None):
-    """key/value [T, Hkv, D] fp16|bf16; slot_mapping [T] int64; caches
-    [NB, Hkv, bs, D] / [NB, Hkv, D, bs] uint8 (FP8) or fp16."""
+class Bound:
+    """An ABI call whose arguments were marshalled once; calling it issues the
+    call again with the same pointers and sizes (the tensors must stay alive)."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = tuple(t(a) if not isinstance(a, (ctypes.c_void_p, type(None))) else a
+                           for t, a in zip(fn.argtypes, args))
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def _write_args(key, value, slot_mapping, key_cache, value_cache, cache_dtype, k_scale, v_scale,
+                stream):
     _need(key, "key", (torch.float16, torch.bfloat16), 3)
     _need(value, "value", key.dtype, 3)
     _need(slot_mapping, "slot_mapping", torch.int64, 1)
     _need(key_cache, "key_cache", ndim=4)
-    _need(value_cache, "value_cache", ndim=4)
+    _need(value_cache, "value_cache", ndim=5)
     nb, hkv, bs, d = key_cache.shape
-    st = _lib.kv_cache_write_fp8(_ptr(key), _ptr(value), TORCH_DTYPES[key.dtype], _ptr(slot_mapping),
-                                 key.shape[0], _ptr(key_cache), _ptr(value_cache),
-                                 _cache_dtype(cache_dtype), nb, bs, hkv, d, _ptr(k_scale),
-                                 _ptr(v_scale), _stream(key.device, stream))
-    _check(st)
+    return [_ptr(key), _ptr(value), TORCH_DTYPES[key.dtype], _ptr(slot_mapping), key.shape[0],
+            _ptr(key_cache), _ptr(value_cache), _cache_dtype(cache_dtype), nb, bs, hkv, d,
+            _ptr(k_scale), _ptr(v_scale), _stream(key.device, stream)]
+
+
+def kv_cache_write_fp8(key, value, slot_mapping, key_cache, value_cache, cache_dtype,
+                       k_scale=None, v_scale=None, stream=None):
+    """key/value [T, Hkv, D] fp16|bf16; slot_mapping [T] int64; caches
+    [NB, Hkv, bs, D] / [NB, Hkv, bs/G, D, G] (G = min(bs, 64)), uint8 (FP8) or
+    fp16."""
+    _check(_lib.kv_cache_write_fp8(*_write_args(key, value, slot_mapping, key_cache, value_cache,
+                                                cache_dtype, k_scale, v_scale, stream)))
+
+
+def bind_kv_cache_write_fp8(key, value, slot_mapping, key_cache, value_cache, cache_dtype,
+                            k_scale=None, v_scale=None, stream=None):
+    args = _write_args(key, value, slot_mapping, key_cache, value_cache, cache_dtype, k_scale,
+                       v_scale, stream)
+    return Bound(_lib.kv_cache_write_fp8, args,
+                 (key, value, slot_mapping, key_cache, value_cache, k_scale, v_scale))
 
 
 def _out(q, out, out_dtype, shape):
@@ -137,11 +164,9 @@ def _out(q, out, out_dtype, shape):
     return out
 
 
-def attn_prefill_paged(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache_dtype,
-                       block_tables, context_lens, max_context_len, softmax_scale,
-                       k_scale=None, v_scale=None, out=None, out_dtype=None, stream=None):
-    """q [total_q, Hq, D]; cu_seqlens_q [B+1] int32; block_tables [B, M] int32;
-    context_lens [B] int32."""
+def _prefill_args(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache_dtype, block_tables,
+                  context_lens, max_context_len, softmax_scale, k_scale, v_scale, out, out_dtype,
+                  stream):
     _need(q, "q", (torch.float16, torch.bfloat16), 3)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
     _need(block_tables, "block_tables", torch.int32, 2)
@@ -149,14 +174,35 @@ def attn_prefill_paged(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache
     total_q, hq, d = q.shape
     nb, hkv, bs, _ = key_cache.shape
     out = _out(q, out, out_dtype, (total_q, hq, d))
-    st = _lib.attn_prefill_paged(
-        _ptr(q), TORCH_DTYPES[q.dtype], _ptr(cu_seqlens_q), block_tables.shape[0], int(max_q_len),
-        total_q, _ptr(key_cache), _ptr(value_cache), _cache_dtype(cache_dtype), bs, nb,
-        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len), hq,
-        hkv, d, _ptr(k_scale), _ptr(v_scale), float(softmax_scale), _ptr(out),
-        TORCH_DTYPES[out.dtype], _stream(q.device, stream))
-    _check(st)
+    args = [_ptr(q), TORCH_DTYPES[q.dtype], _ptr(cu_seqlens_q), block_tables.shape[0],
+            int(max_q_len), total_q, _ptr(key_cache), _ptr(value_cache), _cache_dtype(cache_dtype),
+            bs, nb, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+            int(max_context_len), hq, hkv, d, _ptr(k_scale), _ptr(v_scale), float(softmax_scale),
+            _ptr(out), TORCH_DTYPES[out.dtype], _stream(q.device, stream)]
+    return args, out
+
+
+def attn_prefill_paged(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache_dtype,
+                       block_tables, context_lens, max_context_len, softmax_scale,
+                       k_scale=None, v_scale=None, out=None, out_dtype=None, stream=None):
+    """q [total_q, Hq, D]; cu_seqlens_q [B+1] int32; block_tables [B, M] int32;
+    context_lens [B] int32."""
+    args, out = _prefill_args(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache_dtype,
+                              block_tables, context_lens, max_context_len, softmax_scale,
+                              k_scale, v_scale, out, out_dtype, stream)
+    _check(_lib.attn_prefill_paged(*args))
     return out
+
+
+def bind_attn_prefill_paged(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache_dtype,
+                            block_tables, context_lens, max_context_len, softmax_scale,
+                            k_scale=None, v_scale=None, out=None, out_dtype=None, stream=None):
+    args, out = _prefill_args(q, cu_seqlens_q, max_q_len, key_cache, value_cache, cache_dtype,
+                              block_tables, context_lens, max_context_len, softmax_scale,
+                              k_scale, v_scale, out, out_dtype, stream)
+    return Bound(_lib.attn_prefill_paged, args,
+                 (q, cu_seqlens_q, key_cache, value_cache, block_tables, context_lens, k_scale,
+                  v_scale, out)), out
 
 
 def pa_workspace_bytes(op, batch, q_len, num_q_heads, num_kv_heads, head_dim, num_partitions,
@@ -177,7 +223,7 @@ def pa_supports(op, q_dtype, cache_dtype, head_dim, num_q_heads, num_kv_heads, b
 
 def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_tables, context_lens,
                  max_context_len, softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
-                 out_dtype, stream):
+                 out_dtype, stream, bind=False):
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
     batch = q.shape[0]
@@ -193,10 +239,13 @@ def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_ta
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
             TORCH_DTYPES[out.dtype], _stream(q.device, stream)]
     if op == PA_OP_DECODE:
-        st = fn(_ptr(q), TORCH_DTYPES[q.dtype], batch, *args)
+        args = [_ptr(q), TORCH_DTYPES[q.dtype], batch] + args
     else:
-        st = fn(_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len, *args)
-    _check(st)
+        args = [_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len] + args
+    if bind:
+        return Bound(fn, args, (q, key_cache, value_cache, block_tables, context_lens, k_scale,
+                                v_scale, workspace, out)), out
+    _check(fn(*args))
     return out
 
 
@@ -208,6 +257,28 @@ def attn_decode_paged(q, key_cache, value_cache, cache_dtype, block_tables, cont
     return _decode_like(_lib.attn_decode_paged, PA_OP_DECODE, q, 1, key_cache, value_cache,
                         cache_dtype, block_tables, context_lens, max_context_len, softmax_scale,
                         k_scale, v_scale, num_partitions, workspace, out, out_dtype, stream)
+
+
+def bind_attn_decode_paged(q, key_cache, value_cache, cache_dtype, block_tables, context_lens,
+                           max_context_len, softmax_scale, k_scale=None, v_scale=None,
+                           num_partitions=0, workspace=None, out=None, out_dtype=None,
+                           stream=None):
+    _need(q, "q", (torch.float16, torch.bfloat16), 3)
+    return _decode_like(_lib.attn_decode_paged, PA_OP_DECODE, q, 1, key_cache, value_cache,
+                        cache_dtype, block_tables, context_lens, max_context_len, softmax_scale,
+                        k_scale, v_scale, num_partitions, workspace, out, out_dtype, stream,
+                        bind=True)
+
+
+def bind_attn_verify_paged(q, key_cache, value_cache, cache_dtype, block_tables, context_lens,
+                           max_context_len, softmax_scale, k_scale=None, v_scale=None,
+                           num_partitions=0, workspace=None, out=None, out_dtype=None,
+                           stream=None):
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    return _decode_like(_lib.attn_verify_paged, PA_OP_VERIFY, q, q.shape[1], key_cache,
+                        value_cache, cache_dtype, block_tables, context_lens, max_context_len,
+                        softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
+                        out_dtype, stream, bind=True)
 
 
 def attn_verify_paged(q, key_cache, value_cache, cache_dtype, block_tables, context_lens,

@@ -46,7 +46,8 @@ class DeviceCase:
         cdt = torch.float16 if c.cache_fmt == "f16" else torch.uint8
         nb, hkv, bs, d = c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim
         self.key_cache = torch.empty((nb, hkv, bs, d), dtype=cdt, device=device)
-        self.value_cache = torch.empty((nb, hkv, d, bs), dtype=cdt, device=device)
+        vg = min(bs, 64)   # value groups: dimension-major inside 64-token groups
+        self.value_cache = torch.empty((nb, hkv, bs // vg, d, vg), dtype=cdt, device=device)
         poison_cache(self.key_cache, c.cache_fmt)
         poison_cache(self.value_cache, c.cache_fmt)
         self.max_ctx = int(c.ctx_lens.max()) if len(c.ctx_lens) else 0

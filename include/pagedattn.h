@@ -25,9 +25,14 @@
  *
  * Cache layout (caller-owned device memory; the pages do not fix one):
  *   key_cache   [num_blocks][num_kv_heads][block_size][head_dim]
- *   value_cache [num_blocks][num_kv_heads][head_dim][block_size]
- * i.e. keys are token-major and values dimension-major inside one page of one
- * head. Elements are uint8 FP8 codes (OCP E4M3FN or E5M2) or fp16.
+ *   value_cache [num_blocks][num_kv_heads][block_size / T][head_dim][T],
+ *               T = min(block_size, 64)
+ * i.e. keys are token-major inside one page of one head, and values are
+ * dimension-major inside each group of T consecutive tokens of a page, so the
+ * 64 keys' values a kernel tile needs are one contiguous run. Elements are
+ * uint8 FP8 codes (OCP E4M3FN or E5M2) or fp16. Token o of a page (offset
+ * o = j % block_size) has its value for dimension d at
+ * value_cache[page][h][o / T][d][o % T].
  * Token j of sequence b lives in physical page block_tables[b][j / block_size]
  * at offset j % block_size ("block tables consistently use physical page
  * units", 1.5.0 notes, "Reliability and correctness fixes").

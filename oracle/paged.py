@@ -10,8 +10,10 @@ do not fix a byte layout; the library's documented layout is restated here:
 
 * key cache   ``[num_blocks, num_kv_heads, block_size, head_dim]``
   (token-major inside one page of one head),
-* value cache ``[num_blocks, num_kv_heads, head_dim, block_size]``
-  (dimension-major inside one page of one head).
+* value cache ``[num_blocks, num_kv_heads, block_size // T, head_dim, T]``
+  with ``T = min(block_size, 64)`` (dimension-major inside each group of T
+  consecutive tokens of a page): the value of the token at page offset ``o``,
+  dimension ``d`` is ``value_cache[page, h, o // T, d, o % T]``.
 
 Token j of a sequence lives in physical page ``block_table[j // block_size]``
 at offset ``j % block_size``. A write goes to ``slot = page * block_size +
@@ -30,10 +32,16 @@ E4M3 = fp8.E4M3
 E5M2 = fp8.E5M2
 
 
+def value_group(block_size):
+    """Tokens per dimension-major value group: T = min(block_size, 64)."""
+    return min(int(block_size), 64)
+
+
 def new_caches(num_blocks, num_kv_heads, block_size, head_dim, fmt, fill=0):
     dt = np.float16 if fmt == F16 else np.uint8
+    T = value_group(block_size)
     kc = np.full((num_blocks, num_kv_heads, block_size, head_dim), fill, dtype=dt)
-    vc = np.full((num_blocks, num_kv_heads, head_dim, block_size), fill, dtype=dt)
+    vc = np.full((num_blocks, num_kv_heads, block_size // T, head_dim, T), fill, dtype=dt)
     return kc, vc
 
 
@@ -47,9 +55,10 @@ def quantize(x, fmt, scale=None):
 def write(k, v, slot_mapping, k_cache, v_cache, fmt, k_scale=None, v_scale=None):
     """Quantize-on-write. k, v: [T, Hkv, D]; k_scale, v_scale: [Hkv] float32
     (per KV head) or None. Writes in place, one token at a time."""
-    T, Hkv, D = k.shape
+    ntok, Hkv, D = k.shape
     bs = k_cache.shape[2]
-    for t in range(T):
+    T = value_group(bs)
+    for t in range(ntok):
         slot = int(slot_mapping[t])
         if slot < 0:
             continue
@@ -58,7 +67,7 @@ def write(k, v, slot_mapping, k_cache, v_cache, fmt, k_scale=None, v_scale=None)
             ks = None if k_scale is None else k_scale[h]
             vs = None if v_scale is None else v_scale[h]
             k_cache[page, h, off, :] = quantize(k[t, h, :], fmt, ks)
-            v_cache[page, h, :, off] = quantize(v[t, h, :], fmt, vs)
+            v_cache[page, h, off // T, :, off % T] = quantize(v[t, h, :], fmt, vs)
 
 
 def dequant(codes, fmt, scale=None):
@@ -74,6 +83,7 @@ def gather(k_cache, v_cache, block_table, ctx, g, fmt, k_scale=None, v_scale=Non
     read, so padding entries are never dereferenced."""
     bs = k_cache.shape[2]
     D = k_cache.shape[3]
+    T = value_group(bs)
     if ctx == 0:
         return np.zeros((0, D)), np.zeros((0, D))
     j = np.arange(ctx)
@@ -81,7 +91,7 @@ def gather(k_cache, v_cache, block_table, ctx, g, fmt, k_scale=None, v_scale=Non
     pages = np.asarray(block_table[:used], dtype=np.int64)[j // bs]
     off = j % bs
     k_raw = k_cache[pages, g, off, :]              # [ctx, D]
-    v_raw = v_cache[pages, g, :, off]              # [ctx, D]
+    v_raw = v_cache[pages, g, off // T, :, off % T]  # [ctx, D]
     ks = None if k_scale is None else k_scale[g]
     vs = None if v_scale is None else v_scale[g]
     return dequant(k_raw, fmt, ks), dequant(v_raw, fmt, vs)

@@ -65,6 +65,7 @@ def oracle_cache_heads(case, seqs_heads):
     kc, vc = paged.new_caches(case.num_blocks, case.num_kv_heads, case.block_size,
                               case.head_dim, case.cache_fmt, fill=fill)
     bs = case.block_size
+    T = paged.value_group(bs)
     for b, g in seqs_heads:
         t0, c = int(case.tok_start[b]), int(case.ctx_lens[b])
         slots = case.slot_mapping[t0:t0 + c]
@@ -74,7 +75,7 @@ def oracle_cache_heads(case, seqs_heads):
         ks = None if case.k_scale is None else case.k_scale[g]
         vs = None if case.v_scale is None else case.v_scale[g]
         kc[page, g, off, :] = paged.quantize(k32, case.cache_fmt, ks)
-        vc[page, g, :, off] = paged.quantize(v32, case.cache_fmt, vs)
+        vc[page, g, off // T, :, off % T] = paged.quantize(v32, case.cache_fmt, vs)
     return kc, vc
 
 

@@ -29,6 +29,7 @@ def write_tokens(case, kc, vc, k32, v32, slots):
     """Vectorised form of oracle.paged.write for many tokens at once (the
     per-element arithmetic is oracle.paged.quantize, unchanged)."""
     bs = case.block_size
+    T = paged.value_group(bs)
     keep = slots >= 0
     slots = slots[keep]
     page, off = slots // bs, slots % bs
@@ -36,7 +37,7 @@ def write_tokens(case, kc, vc, k32, v32, slots):
     vq = paged.quantize(v32[keep], case.cache_fmt, None if case.v_scale is None else case.v_scale[None, :, None])
     for h in range(case.num_kv_heads):
         kc[page, h, off, :] = kq[:, h, :]
-        vc[page, h, :, off] = vq[:, h, :]
+        vc[page, h, off // T, :, off % T] = vq[:, h, :]
 
 
 def q_f32(case):

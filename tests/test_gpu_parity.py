@@ -42,6 +42,11 @@ WRITE_CASES = [
     ("e5m2", "f16", 64, 64, (130, 17)),
     ("e5m2", "bf16", 32, 128, (77,)),
     ("f16", "f16", 16, 64, (65, 33)),
+    # fewer than 64 tokens: one thread per 16-element chunk
+    ("e4m3", "f16", 16, 128, (5, 17, 1)),
+    ("e5m2", "bf16", 2048, 64, (3,)),
+    ("f16", "f16", 32, 128, (2, 9)),
+    ("e4m3", "bf16", 64, 128, (63,)),
 ]
 
 
@@ -78,7 +83,7 @@ def test_write_every_fp16_pattern(runner, fmt, scale):
     k = torch.from_numpy(x.copy()).to(dev)
     v = torch.from_numpy(x[::-1].copy()).to(dev)
     kc = torch.full((nb, 1, bs, D), 0x7F, dtype=torch.uint8, device=dev)
-    vc = torch.full((nb, 1, D, bs), 0x7F, dtype=torch.uint8, device=dev)
+    vc = torch.full((nb, 1, 1, D, bs), 0x7F, dtype=torch.uint8, device=dev)
     sc = None if scale is None else torch.tensor([scale], dtype=torch.float32, device=dev)
     pa.kv_cache_write_fp8(k, v, torch.from_numpy(slots).to(dev), kc, vc, fmt, sc, sc)
     torch.cuda.synchronize()

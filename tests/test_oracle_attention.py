@@ -338,7 +338,7 @@ def test_planted_attention_mistakes_fail_the_library_check(monkeypatch, mutant):
             bs = kc.shape[2]
             j = np.arange(ctx)
             pages = np.asarray(bt[:-(-ctx // bs)], dtype=np.int64)[j // bs]
-            raw = vc.reshape(vc.shape[0], vc.shape[1], bs, -1)[pages, g, j % bs, :]
+            raw = vc.reshape(vc.shape[0], vc.shape[1], bs, -1)[pages, g, j % bs, :]   # token-major reading
             return K, paged.dequant(raw, fmt, None if vs is None else vs[g])
         monkeypatch.setattr(paged, "gather", gather_vt)
     o, _, _ = _oracle(case)
