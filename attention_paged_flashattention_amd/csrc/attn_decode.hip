@@ -73,6 +73,8 @@ __device__ __forceinline__ half8 val_op(const uint32_t* dw) {
 }
 
 constexpr float kNegInf = -__builtin_inff();
+// Growth of the running max (log2 units) tolerated before O and l are rescaled.
+constexpr float kRescaleSlackD = 8.0f;
 
 // Raw cache bytes of one 64-key tile as one lane holds them.
 template <int D, int ES>
@@ -284,9 +286,17 @@ void decode_split_kernel(const DecodeArgs a) {
         for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sacc[nb][s][i]);
       tm = fmaxf(tm, lane_xor(tm, 16));
       tm = fmaxf(tm, lane_xor(tm, 32));
-      const float mnew = fmaxf(m[nb], tm * C);
-      const float muse = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[nb] - muse);
+      // Lazy rescaling (see the prefill kernel): the reference max is raised
+      // only when some row's max exceeds it by more than 2^8.
+      const float mcand = fmaxf(m[nb], tm * C);
+      if (__any(mcand > m[nb] + kRescaleSlackD)) {
+        const float alpha = mcand == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(m[nb] - mcand);
+        m[nb] = mcand;
+        l[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[nb][db] *= alpha;
+      }
+      const float muse = m[nb] == kNegInf ? 0.0f : m[nb];
       float ps = 0.0f;
       half8 pop[2];
 #pragma unroll
@@ -298,11 +308,9 @@ void decode_split_kernel(const DecodeArgs a) {
           pop[s >> 1][(s & 1) * 4 + i] = (_Float16)pv;
         }
       }
-      l[nb] = l[nb] * alpha + ps;
-      m[nb] = mnew;
+      l[nb] += ps;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        o[nb][db] *= alpha;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           half8 vop = val_op<FMT>(&T.v[db][hh * (8 * ES / 4)]);

@@ -7,24 +7,30 @@
 // several query heads onto one KV head's tensor-core work, measured in
 // useful causal FLOP/s). How it is done here (gfx950):
 //
-// * Work-group = 128 rows that share one KV head: 128/G query tokens x the G
-//   query heads of that KV head (GQA packing), 4 waves x 32 rows.
+// * Work-group = 256 rows that share one KV head: 256/G query tokens x the G
+//   query heads of that KV head (GQA packing), 8 waves x 32 rows, two waves
+//   per SIMD.
 // * The grid is ordered so that consecutive work-groups take consecutive KV
 //   heads: with round-robin dispatch over the 8 XCDs, each XCD's L2 holds the
 //   K/V of one head while all its work-groups stream it. Query tiles with the
 //   most keys are dispatched first.
-// * Keys are walked in 64-key tiles. 256 threads load the FP8 tile with
+// * Keys are walked in 64-key tiles. The 512 threads load the FP8 tile with
 //   128-bit loads (page id per 16-key run), dequantize in registers and store
-//   16-bit K (token-major) and V (dimension-major) tiles in LDS, double
-//   buffered, one barrier per tile; the next tile's global loads are in
-//   flight while the current tile is multiplied.
+//   16-bit K (token-major) and V (dimension-major) tiles in LDS, three
+//   buffers deep; the tile after next is in flight from HBM while the current
+//   one is multiplied.
+// * Ping-pong: waves 0-3 and 4-7 share the SIMDs and cross the same two
+//   barriers per tile doing opposite work, so one wave's softmax (VALU) runs
+//   under the other wave's MFMAs.
 // * S^T = K Q^T on v_mfma_f32_32x32x16 (keys on M, query rows on N, Q held in
 //   registers), FP32 accumulation. Keys are assigned to MFMA rows with bits 2
 //   and 3 of the row index swapped, which makes each lane's S^T outputs the
 //   8-key runs that the PV step needs as its B operand: P never leaves the
 //   lane, and the V^T operand is one 16-byte LDS read.
 // * Online softmax in exp2 units, the row max reduced between the two lanes
-//   that share a row; only tiles that cross the causal diagonal are masked.
+//   that share a row; O is rescaled only when a row's max grows by more than
+//   2^8 (wave vote), so most tiles skip the rescale; only tiles that cross the
+//   causal diagonal are masked.
 // * P is rounded to fp16 (V from FP8 is exact in fp16) and O^T += V^T P^T runs
 //   on v_mfma_f32_32x32x16_f16.
 #include "pa_device.h"
@@ -48,6 +54,8 @@ __device__ __forceinline__ f32x16 mfma32_qk(typename QOp32<QT>::T a, typename QO
 }
 
 constexpr float kNegInfP = -__builtin_inff();
+// Growth of the running max (log2 units) tolerated before O and l are rescaled.
+constexpr float kRescaleSlack = 8.0f;
 
 // MFMA row R of a 32-key block holds key kappa(R): bits 2 and 3 swapped.
 __device__ __forceinline__ int kappa(int R) {
@@ -55,19 +63,26 @@ __device__ __forceinline__ int kappa(int R) {
 }
 
 template <int D, int FMT, int QT, int OT>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(const PrefillArgs a) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
   constexpr int BN = 64;                  // keys per tile
+  constexpr int NBUF = 3;                 // LDS tile buffers
   constexpr int KPAD = D + 8;             // K tile row stride (16-bit elements)
   constexpr int VPAD = BN + 8;            // V tile row stride
   constexpr int KS = D / 16;              // QK k-steps (16 dims each)
   constexpr int DBLK = D / 32;            // 32-dim output blocks
-  constexpr int EPT = D / 4;              // elements per thread per tile (K and V)
-  constexpr int TPR = 256 / D;            // threads per V row (dimension)
+  constexpr int NT = kPrefillThreads;
+  // elements per staging thread per tile (K and V): at least one 16-byte load
+  constexpr int EPT = (BN * D / NT) * ES >= 16 ? BN * D / NT : 16 / ES;
+  constexpr int NSTAGE = BN * D / EPT;    // staging threads (whole waves)
+  constexpr int TPK = D / EPT;            // threads per key row
+  constexpr int TPR = BN / EPT;           // threads per value row (dimension)
+  static_assert(NSTAGE % 64 == 0 && NSTAGE <= NT, "staging uses whole waves");
   using OpT = typename QOp32<QT>::T;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][BN * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * VPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF][BN * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][D * VPAD];
 
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
@@ -90,6 +105,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  const bool grp_b = w >= 4;              // ping-pong group: waves 0-3 (A), 4-7 (B)
   const int c32 = lane & 31, hgrp = lane >> 5;
   const int bs_log2 = a.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
@@ -112,16 +128,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       qop[ks] = rvalid ? __builtin_bit_cast(OpT, ld16(qp + 16 * ks)) : OpT{};
   }
 
-  // ---- global -> register staging of one tile ----
-  // K: thread owns key kt = tid / 4, dims kd0 .. kd0 + EPT - 1.
-  // V: thread owns dim vd = tid / TPR, keys vk0 .. vk0 + EPT - 1.
-  const int kt = tid >> 2, kd0 = (tid & 3) * EPT;
+  // ---- global -> register staging (all 512 threads) ----
+  // K: thread owns key kt, dims kd0 .. kd0 + EPT - 1.
+  // V: thread owns dim vd, keys vk0 .. vk0 + EPT - 1.
+  // Keys past the context are not loaded (zeros), so no stale slot -- NaN
+  // included -- reaches the tiles.
+  const int kt = tid / TPK, kd0 = (tid % TPK) * EPT;
   const int vd = tid / TPR, vk0 = (tid % TPR) * EPT;
   constexpr int KLD = EPT * ES / 16;      // 16-byte loads for K
   constexpr int VLD = EPT * ES / 16;      // 16-byte loads for V
+  constexpr int KPL = 16 / ES;            // keys per 16-byte value load
   u32x4 kreg[KLD], vreg[VLD];
 
-  auto load_tile = [&](int t0) {
+  const bool stager = tid < NSTAGE;
+  auto load_kv = [&](int t0) {
+    if (!stager) return;
     const int key = t0 + kt;
     if (key < ctx) {
       const int64_t page = btb[key >> bs_log2];
@@ -133,8 +154,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < KLD; ++x) kreg[x] = u32x4{0, 0, 0, 0};
     }
-    // V: each 16-byte load covers 16 / ES consecutive keys of dimension vd
-    constexpr int KPL = 16 / ES;
 #pragma unroll
     for (int x = 0; x < VLD; ++x) {
       const int k0 = t0 + vk0 + x * KPL;
@@ -147,7 +166,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         u32x4 v = ld16(vp);
         const int nvalid = ctx - k0;
         if (nvalid < KPL) {
-          // zero elements of keys past the context (select; slots may be NaN)
           uint32_t e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int i = 0; i < KPL; ++i) {
@@ -165,8 +183,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* kdst = &sk[buf][kt * KPAD + kd0];
+  // Key kt is stored in LDS row kappa(kt) of its 32-key block (kappa is its own
+  // inverse), so the MFMA operand read of row R is unpermuted and consecutive
+  // lanes hit consecutive rows.
+  const int kt_row = (kt & ~31) | kappa(kt & 31);
+  auto store_kv = [&](int buf) {
+    if (!stager) return;
+    uint16_t* kdst = &sk[buf][kt_row * KPAD + kd0];
     uint16_t* vdst = &sv[buf][vd * VPAD + vk0];
     if constexpr (FMT == KV_F16) {
 #pragma unroll
@@ -192,38 +215,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
   };
 
+  // S^T = K Q^T for the two 32-key blocks of the tile in buffer kb. K operands
+  // are read from LDS PF reads ahead of the MFMA that consumes them.
+  constexpr int NQK = KS * 2;  // (ks, mb) pairs
+  constexpr int PF = 4;
+  f32x16 sacc[2];
+  auto qk = [&](int kb) {
+    const uint16_t* skb = sk[kb] + c32 * KPAD + 8 * hgrp;
+    auto rd = [&](int i) {  // i = ks * 2 + mb
+      return *reinterpret_cast<const OpT*>(skb + (i & 1) * 32 * KPAD + 16 * (i >> 1));
+    };
+    OpT ring[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ring[i] = rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const OpT kop = ring[i % PF];
+      if (i + PF < NQK) ring[i % PF] = rd(i + PF);
+      sacc[i & 1] = mfma32_qk<QT>(kop, qop[i >> 1], sacc[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the read PF ahead of its MFMA
+    }
+  };
+
   float m = kNegInfP, l = 0.0f;
   f32x16 oacc[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+  half8 pop[4];
 
-  const int krow0 = kappa(c32);  // K tile row this lane feeds for MFMA row c32
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
-    const int t0 = n * BN;
-    if (n + 1 < ntiles) load_tile(t0 + BN);
-
-    const uint16_t* skb = sk[buf];
-    const uint16_t* svb = sv[buf];
-
-    // S^T = K Q^T for two 32-key blocks.
-    f32x16 sacc[2];
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        OpT kop = *reinterpret_cast<const OpT*>(skb + (mb * 32 + krow0) * KPAD + 16 * ks + 8 * hgrp);
-        sacc[mb] = mfma32_qk<QT>(kop, qop[ks], sacc[mb]);
-      }
-    }
-
+  // Softmax of tile n (keys t0 .. t0+63, S in sacc) into P (fp16).
+  auto softmax = [&](int t0) {
     // Keys held by this lane: block mb, register j -> MFMA row
     // R = 8 (j/4) + 4 hgrp + j%4 -> key t0 + 32 mb + kappa(R)
     //   = t0 + 32 mb + 16 (j/8) + 8 hgrp + 4 ((j/4)&1) + j%4.
@@ -236,19 +260,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
           if (key > rpos || key >= ctx) sacc[mb][j] = kNegInfP;
         }
     }
-
     float tm = kNegInfP;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sacc[mb][j]);
     tm = fmaxf(tm, lane_xor(tm, 32));
-    const float mnew = fmaxf(m, tm * C);
-    const float muse = mnew == kNegInfP ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - muse);
-    m = mnew;
+    // Lazy rescaling: O and l are kept relative to a running max m that is
+    // raised only when some row of the wave sees a max larger than m + 8
+    // (log2 units). p = 2^(s*C - m) then stays <= 2^8 (fine in fp16), and O/l
+    // is unchanged because both carry the same reference.
+    const float mcand = fmaxf(m, tm * C);
+    if (__any(mcand > m + kRescaleSlack)) {
+      const float alpha = mcand == kNegInfP ? 1.0f : __builtin_amdgcn_exp2f(m - mcand);
+      m = mcand;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+    }
+    const float muse = m == kNegInfP ? 0.0f : m;
     float ps = 0.0f;
-    half8 pop[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -257,21 +288,69 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         ps += pv;
         pop[mb * 2 + (j >> 3)][j & 7] = (_Float16)pv;
       }
-    l = l * alpha + ps;
+    l += ps;
+  };
 
+  // O^T += V^T P^T with V from buffer vb, operands read PF ahead.
+  auto pv = [&](int vb) {
+    const uint16_t* svb = sv[vb] + c32 * VPAD + 8 * hgrp;
+    auto rdv = [&](int i) {  // i = db * 4 + kk
+      return *reinterpret_cast<const half8*>(svb + (i >> 2) * 32 * VPAD + 16 * (i & 3));
+    };
+    constexpr int NPV = DBLK * 4;
+    half8 vring[PF];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      oacc[db] *= alpha;
+    for (int i = 0; i < PF; ++i) vring[i] = rdv(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        half8 vop = *reinterpret_cast<const half8*>(svb + (db * 32 + c32) * VPAD + 16 * kk + 8 * hgrp);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[kk], oacc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < NPV; ++i) {
+      const half8 vop = vring[i % PF];
+      if (i + PF < NPV) vring[i % PF] = rdv(i + PF);
+      oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop[i & 3], oacc[i >> 2], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    if (n + 1 < ntiles) store_tile(buf ^ 1);
+  // Ping-pong schedule. Both wave groups cross the same barriers but do
+  // opposite work between them, so on every SIMD one wave runs softmax (VALU)
+  // while the other runs MFMAs:
+  //   phase 1 of tile n:  A softmax(n)            | B PV(n-1), QK(n)
+  //   phase 2 of tile n:  A PV(n), QK(n+1)        | B softmax(n)
+  // Tile n sits in LDS buffer n % 3 from phase 2 of tile n-1 (A's QK) to
+  // phase 1 of tile n+1 (B's PV). Tile n+2 is loaded from HBM during phase 1
+  // of tile n and written to buffer (n+2) % 3 in phase 2, after the barrier
+  // that retires its last reader (B's PV of tile n-1).
+  load_kv(0);
+  store_kv(0);
+  if (ntiles > 1) {
+    load_kv(BN);
+    store_kv(1);
+  }
+  __syncthreads();
+  if (!grp_b) qk(0);
+  __syncthreads();
+  for (int n = 0; n < ntiles; ++n) {
+    const bool stage = n + 2 < ntiles;
+    if (stage) load_kv((n + 2) * BN);
+    // phase 1
+    if (!grp_b) {
+      softmax(n * BN);
+    } else {
+      if (n > 0) pv((n - 1) % NBUF);
+      qk(n % NBUF);
+    }
+    __syncthreads();
+    // phase 2
+    if (stage) store_kv((n + 2) % NBUF);
+    if (!grp_b) {
+      pv(n % NBUF);
+      if (n + 1 < ntiles) qk((n + 1) % NBUF);
+    } else {
+      softmax(n * BN);
+    }
     __syncthreads();
   }
+  if (grp_b) pv((ntiles - 1) % NBUF);
 
   // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r].
   l += lane_xor(l, 32);
@@ -291,7 +370,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 template <int D, int FMT, int QT>
 static void launch_pf(const PrefillArgs& a, int ot, hipStream_t s) {
   const unsigned nblk = (unsigned)((int64_t)a.num_kv_heads * a.q_blocks * a.batch);
-  dim3 grid(nblk), block(256);
+  dim3 grid(nblk), block(kPrefillThreads);
   if (ot == O_F32) hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_F32>), grid, block, 0, s, a);
   else if (ot == O_F16) hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_F16>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_BF16>), grid, block, 0, s, a);

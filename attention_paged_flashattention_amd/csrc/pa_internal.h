@@ -79,7 +79,9 @@ hipError_t launch_decode(const DecodeArgs& a, int batch, int head_dim, int fmt, 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int fmt, int qt, int ot,
                           hipStream_t stream);
 
-// Rows of the prefill work-group tile (query tokens x heads of one KV group).
-constexpr int kPrefillRows = 128;
+// Rows of the prefill work-group tile (query tokens x heads of one KV group)
+// and its threads (8 waves of 32 rows).
+constexpr int kPrefillRows = 256;
+constexpr int kPrefillThreads = 512;
 
 }  // namespace pa

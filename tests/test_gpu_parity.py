@@ -163,7 +163,9 @@ def test_verify_rows_equal_decodes(runner):
         ctx_i = dc.ctx_lens - 7 + i
         od = dc.decode(q=qv[:, i].contiguous(), ctx_lens=ctx_i.contiguous(),
                        max_ctx=int(case.ctx_lens.max()), out_dtype=torch.float32)
-        assert torch.max(torch.abs(od - out[:, i])).item() < 1e-5
+        # same kernels; P is rounded to fp16 against each launch's own running
+        # max, so the two agree to fp16 rounding of P, far inside the tolerance
+        assert torch.max(torch.abs(od - out[:, i])).item() < 1e-4
 
 
 def test_decode_empty_context_rows_are_zero(runner):
@@ -200,8 +202,10 @@ def test_decode_partition_count_invariance(runner):
     dc = runner.DeviceCase(case)
     dc.write_all()
     outs = [dc.decode(num_partitions=p, out_dtype=torch.float32) for p in (1, 2, 5, 16, 94)]
+    # each partitioning rounds P to fp16 against its own running maxima, so
+    # results agree to fp16 rounding of P (far inside the oracle tolerance)
     for o in outs[1:]:
-        assert torch.max(torch.abs(o - outs[0])).item() < 2e-5
+        assert torch.max(torch.abs(o - outs[0])).item() < 1e-4
 
 
 # ---------------------------------------------------------------------------
