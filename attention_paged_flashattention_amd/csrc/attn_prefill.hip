@@ -17,8 +17,7 @@
 // * Keys are walked in 64-key tiles. The 512 threads load the FP8 tile with
 //   128-bit loads (page id per 16-key run), dequantize in registers and store
 //   16-bit K (token-major) and V (dimension-major) tiles in LDS, three
-//   buffers deep; the tile after next is in flight from HBM while the current
-//   one is multiplied.
+//   buffers deep; loads run three tiles ahead of the tile being multiplied.
 // * Ping-pong: waves 0-3 and 4-7 share the SIMDs and cross the same two
 //   barriers per tile doing opposite work, so one wave's softmax (VALU) runs
 //   under the other wave's MFMAs.
@@ -138,27 +137,32 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int KLD = EPT * ES / 16;      // 16-byte loads for K
   constexpr int VLD = EPT * ES / 16;      // 16-byte loads for V
   constexpr int KPL = 16 / ES;            // keys per 16-byte value load
-  u32x4 kreg[KLD], vreg[VLD];
-
   const bool stager = tid < NSTAGE;
-  auto load_kv = [&](int t0) {
+  struct Stage {
+    u32x4 k[KLD], v[VLD];
+  };
+  const bool uni = bs_log2 >= 6;          // a 64-key tile lies in one page
+
+  auto load_kv = [&](Stage& R, int t0) __attribute__((always_inline)) {
     if (!stager) return;
+    // one uniform page-id load per tile when pages hold >= 64 keys
+    const int64_t tpage = uni ? (int64_t)btb[t0 >> bs_log2] : 0;
     const int key = t0 + kt;
     if (key < ctx) {
-      const int64_t page = btb[key >> bs_log2];
+      const int64_t page = uni ? tpage : (int64_t)btb[key >> bs_log2];
       const uint8_t* kp = a.key_cache +
           (((page * kvh + g) << bs_log2) + (key & bs_mask)) * (int64_t)(D * ES) + kd0 * ES;
 #pragma unroll
-      for (int x = 0; x < KLD; ++x) kreg[x] = ld16(kp + 16 * x);
+      for (int x = 0; x < KLD; ++x) R.k[x] = ld16(kp + 16 * x);
     } else {
 #pragma unroll
-      for (int x = 0; x < KLD; ++x) kreg[x] = u32x4{0, 0, 0, 0};
+      for (int x = 0; x < KLD; ++x) R.k[x] = u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int x = 0; x < VLD; ++x) {
       const int k0 = t0 + vk0 + x * KPL;
       if (k0 < ctx) {
-        const int64_t page = btb[k0 >> bs_log2];
+        const int64_t page = uni ? tpage : (int64_t)btb[k0 >> bs_log2];
         const int vo = k0 & bs_mask;  // values: dimension-major inside 2^vg_log2-token groups
         const uint8_t* vp = a.value_cache +
             (((((page * kvh + g) << (bs_log2 - vg_log2)) + (vo >> vg_log2)) * D + vd) << vg_log2 |
@@ -176,9 +180,9 @@ void prefill_kernel(const PrefillArgs a) {
           }
           v = u32x4{e[0], e[1], e[2], e[3]};
         }
-        vreg[x] = v;
+        R.v[x] = v;
       } else {
-        vreg[x] = u32x4{0, 0, 0, 0};
+        R.v[x] = u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -187,30 +191,30 @@ void prefill_kernel(const PrefillArgs a) {
   // inverse), so the MFMA operand read of row R is unpermuted and consecutive
   // lanes hit consecutive rows.
   const int kt_row = (kt & ~31) | kappa(kt & 31);
-  auto store_kv = [&](int buf) {
+  auto store_kv = [&](const Stage& R, int buf) __attribute__((always_inline)) {
     if (!stager) return;
     uint16_t* kdst = &sk[buf][kt_row * KPAD + kd0];
     uint16_t* vdst = &sv[buf][vd * VPAD + vk0];
     if constexpr (FMT == KV_F16) {
 #pragma unroll
-      for (int x = 0; x < KLD; ++x) *reinterpret_cast<u32x4*>(kdst + 8 * x) = kreg[x];
+      for (int x = 0; x < KLD; ++x) *reinterpret_cast<u32x4*>(kdst + 8 * x) = R.k[x];
 #pragma unroll
-      for (int x = 0; x < VLD; ++x) *reinterpret_cast<u32x4*>(vdst + 8 * x) = vreg[x];
+      for (int x = 0; x < VLD; ++x) *reinterpret_cast<u32x4*>(vdst + 8 * x) = R.v[x];
     } else {
 #pragma unroll
       for (int x = 0; x < KLD; ++x) {
         if constexpr (QT == Q_BF16) {
-          *reinterpret_cast<bf16x8*>(kdst + 16 * x) = fp8x8_to_bf16x8<FMT>(kreg[x].x, kreg[x].y);
-          *reinterpret_cast<bf16x8*>(kdst + 16 * x + 8) = fp8x8_to_bf16x8<FMT>(kreg[x].z, kreg[x].w);
+          *reinterpret_cast<bf16x8*>(kdst + 16 * x) = fp8x8_to_bf16x8<FMT>(R.k[x].x, R.k[x].y);
+          *reinterpret_cast<bf16x8*>(kdst + 16 * x + 8) = fp8x8_to_bf16x8<FMT>(R.k[x].z, R.k[x].w);
         } else {
-          *reinterpret_cast<half8*>(kdst + 16 * x) = fp8x8_to_half8<FMT>(kreg[x].x, kreg[x].y);
-          *reinterpret_cast<half8*>(kdst + 16 * x + 8) = fp8x8_to_half8<FMT>(kreg[x].z, kreg[x].w);
+          *reinterpret_cast<half8*>(kdst + 16 * x) = fp8x8_to_half8<FMT>(R.k[x].x, R.k[x].y);
+          *reinterpret_cast<half8*>(kdst + 16 * x + 8) = fp8x8_to_half8<FMT>(R.k[x].z, R.k[x].w);
         }
       }
 #pragma unroll
       for (int x = 0; x < VLD; ++x) {
-        *reinterpret_cast<half8*>(vdst + 16 * x) = fp8x8_to_half8<FMT>(vreg[x].x, vreg[x].y);
-        *reinterpret_cast<half8*>(vdst + 16 * x + 8) = fp8x8_to_half8<FMT>(vreg[x].z, vreg[x].w);
+        *reinterpret_cast<half8*>(vdst + 16 * x) = fp8x8_to_half8<FMT>(R.v[x].x, R.v[x].y);
+        *reinterpret_cast<half8*>(vdst + 16 * x + 8) = fp8x8_to_half8<FMT>(R.v[x].z, R.v[x].w);
       }
     }
   };
@@ -220,7 +224,7 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int NQK = KS * 2;  // (ks, mb) pairs
   constexpr int PF = 4;
   f32x16 sacc[2];
-  auto qk = [&](int kb) {
+  auto qk = [&](int kb) __attribute__((always_inline)) {
     const uint16_t* skb = sk[kb] + c32 * KPAD + 8 * hgrp;
     auto rd = [&](int i) {  // i = ks * 2 + mb
       return *reinterpret_cast<const OpT*>(skb + (i & 1) * 32 * KPAD + 16 * (i >> 1));
@@ -247,7 +251,7 @@ void prefill_kernel(const PrefillArgs a) {
   half8 pop[4];
 
   // Softmax of tile n (keys t0 .. t0+63, S in sacc) into P (fp16).
-  auto softmax = [&](int t0) {
+  auto softmax = [&](int t0) __attribute__((always_inline)) {
     // Keys held by this lane: block mb, register j -> MFMA row
     // R = 8 (j/4) + 4 hgrp + j%4 -> key t0 + 32 mb + kappa(R)
     //   = t0 + 32 mb + 16 (j/8) + 8 hgrp + 4 ((j/4)&1) + j%4.
@@ -292,7 +296,7 @@ void prefill_kernel(const PrefillArgs a) {
   };
 
   // O^T += V^T P^T with V from buffer vb, operands read PF ahead.
-  auto pv = [&](int vb) {
+  auto pv = [&](int vb) __attribute__((always_inline)) {
     const uint16_t* svb = sv[vb] + c32 * VPAD + 8 * hgrp;
     auto rdv = [&](int i) {  // i = db * 4 + kk
       return *reinterpret_cast<const half8*>(svb + (i >> 2) * 32 * VPAD + 16 * (i & 3));
@@ -317,21 +321,24 @@ void prefill_kernel(const PrefillArgs a) {
   //   phase 1 of tile n:  A softmax(n)            | B PV(n-1), QK(n)
   //   phase 2 of tile n:  A PV(n), QK(n+1)        | B softmax(n)
   // Tile n sits in LDS buffer n % 3 from phase 2 of tile n-1 (A's QK) to
-  // phase 1 of tile n+1 (B's PV). Tile n+2 is loaded from HBM during phase 1
-  // of tile n and written to buffer (n+2) % 3 in phase 2, after the barrier
-  // that retires its last reader (B's PV of tile n-1).
-  load_kv(0);
-  store_kv(0);
+  // phase 1 of tile n+1 (B's PV). Tile n+3's HBM loads are issued at the top of
+  // tile n into one of two register sets; tile n+2 (loaded a tile earlier) is
+  // written to buffer (n+2) % 3 in phase 2, after the barrier that retires its
+  // last reader (B's PV of tile n-1).
+  Stage R0, R1;
+  load_kv(R0, 0);
+  store_kv(R0, 0);
   if (ntiles > 1) {
-    load_kv(BN);
-    store_kv(1);
+    load_kv(R1, BN);
+    store_kv(R1, 1);
   }
+  if (ntiles > 2) load_kv(R0, 2 * BN);
   __syncthreads();
   if (!grp_b) qk(0);
   __syncthreads();
-  for (int n = 0; n < ntiles; ++n) {
-    const bool stage = n + 2 < ntiles;
-    if (stage) load_kv((n + 2) * BN);
+  // Rl receives tile n+3, Rs holds tile n+2.
+  auto iteration = [&](int n, Stage& Rl, const Stage& Rs) __attribute__((always_inline)) {
+    if (n + 3 < ntiles) load_kv(Rl, (n + 3) * BN);
     // phase 1
     if (!grp_b) {
       softmax(n * BN);
@@ -341,7 +348,7 @@ void prefill_kernel(const PrefillArgs a) {
     }
     __syncthreads();
     // phase 2
-    if (stage) store_kv((n + 2) % NBUF);
+    if (n + 2 < ntiles) store_kv(Rs, (n + 2) % NBUF);
     if (!grp_b) {
       pv(n % NBUF);
       if (n + 1 < ntiles) qk((n + 1) % NBUF);
@@ -349,6 +356,10 @@ void prefill_kernel(const PrefillArgs a) {
       softmax(n * BN);
     }
     __syncthreads();
+  };
+  for (int n = 0; n < ntiles; n += 2) {
+    iteration(n, R1, R0);
+    if (n + 1 < ntiles) iteration(n + 1, R0, R1);
   }
   if (grp_b) pv((ntiles - 1) % NBUF);
 
