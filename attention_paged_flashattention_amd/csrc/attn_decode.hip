@@ -398,18 +398,37 @@ void decode_split_kernel(const DecodeArgs a) {
 //   out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
 // over the partitions in index order; empty partitions (m_p = -inf) weigh 0.
 // Times the per-head value scale. A row with no visible key is written as zeros.
-// The partition weights are computed once into LDS; each thread then sums a
-// fixed slice of partitions for one head dimension, and the slices are added
-// in a fixed order, so the result does not depend on timing.
+// The partition weights go to LDS first (one load per partition, spread over
+// the threads). Thread (slice sl, dimension group dg) then adds the weighted
+// partials of partitions sl, sl + SL, ... for dimensions 4dg..4dg+3, issuing
+// kCombineBatch 16-byte loads before the first add; slices are summed in a
+// fixed order, so the result does not depend on timing.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineBatch = 8;
 constexpr int kMaxCombineParts = 4096;
+
+__device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_max) {
+  // wave64 butterfly, then the 4 wave results in order
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    const float o = lane_xor(v, m);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))
+                : (red[0] + red[1]) + (red[2] + red[3]);
+}
 
 template <int D, int FMT, int OT>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const DecodeArgs a) {
-  constexpr int SL = kCombineThreads / D;  // partition slices (2 at D = 128, 4 at D = 64)
+  constexpr int DG = D / 4;                   // dimension groups of 4
+  constexpr int SL = kCombineThreads / DG;    // partition slices (8 at D = 128, 16 at D = 64)
   __shared__ float sw[kMaxCombineParts];
-  __shared__ float sred[kCombineThreads];
-  __shared__ float sacc[SL][D];
+  __shared__ float red[4];
+  __shared__ f32x4 sacc[SL][DG];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -419,54 +438,45 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   const float* ml = a.ws_ml + row * P * 2;
   const float* po = a.ws_o + row * P * D;
 
-  float M = kNegInf;
-  for (int p = t; p < P; p += kCombineThreads) M = fmaxf(M, ml[2 * p]);
-  sred[t] = M;
-  __syncthreads();
-  for (int s = kCombineThreads / 2; s > 0; s >>= 1) {
-    if (t < s) sred[t] = fmaxf(sred[t], sred[t + s]);
-    __syncthreads();
-  }
-  M = sred[0];
-  __syncthreads();
-  float lsum = 0.0f;
+  float mloc = kNegInf;
+  for (int p = t; p < P; p += kCombineThreads) mloc = fmaxf(mloc, ml[2 * p]);
+  const float M = block_reduce_256(mloc, red, true);
+  float lloc = 0.0f;
   for (int p = t; p < P; p += kCombineThreads) {
     const float mp = ml[2 * p];
     const float wt = (mp == kNegInf || M == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
     sw[p] = wt;
-    lsum += wt * ml[2 * p + 1];
+    lloc += wt * ml[2 * p + 1];
   }
-  sred[t] = lsum;
-  __syncthreads();
-  for (int s = kCombineThreads / 2; s > 0; s >>= 1) {
-    if (t < s) sred[t] += sred[t + s];
-    __syncthreads();
-  }
-  const float L = sred[0];
+  const float L = block_reduce_256(lloc, red, false);   // its barriers also publish sw
 
-  const int d = t % D, sl = t / D;
-  const int per = (P + SL - 1) / SL;
-  const int p0 = sl * per, p1 = min(P, p0 + per);
-  float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
-  int p = p0;
-  for (; p + 4 <= p1; p += 4) {
-    const float o0 = po[(int64_t)p * D + d], o1 = po[(int64_t)(p + 1) * D + d];
-    const float o2 = po[(int64_t)(p + 2) * D + d], o3 = po[(int64_t)(p + 3) * D + d];
-    acc0 += sw[p] * o0;
-    acc1 += sw[p + 1] * o1;
-    acc2 += sw[p + 2] * o2;
-    acc3 += sw[p + 3] * o3;
+  const int dg = t % DG, sl = t / DG;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int pb = sl; pb < P; pb += SL * kCombineBatch) {
+    f32x4 ov[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int p = pb + k * SL;
+      ov[k] = p < P ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * D + 4 * dg)
+                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int p = pb + k * SL;
+      const float wt = p < P ? sw[p] : 0.0f;
+      acc += wt * ov[k];
+    }
   }
-  for (; p < p1; ++p) acc0 += sw[p] * po[(int64_t)p * D + d];
-  sacc[sl][d] = (acc0 + acc1) + (acc2 + acc3);
+  sacc[sl][dg] = acc;
   __syncthreads();
   if (sl == 0) {
-    float acc = 0.0f;
+    f32x4 o = sacc[0][dg];
 #pragma unroll
-    for (int k = 0; k < SL; ++k) acc += sacc[k][d];
+    for (int k = 1; k < SL; ++k) o += sacc[k][dg];
     const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
     const float f = L > 0.0f ? vscale / L : 0.0f;
-    store_out<OT>(a.out, row * D + d, acc * f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_out<OT>(a.out, row * D + 4 * dg + i, o[i] * f);
   }
 }
 

@@ -8,9 +8,9 @@
 // overwritten in full, and the attention kernels never read a slot past the
 // context.
 //
-// Each thread quantizes 16 consecutive head dimensions of one token's K and V.
-// Large writes (prefill chunks) put consecutive tokens on consecutive lanes;
-// small writes (a decode step) put every chunk of every head on its own thread.
+// Large writes (prefill chunks): each thread quantizes 16 consecutive head
+// dimensions of one token's K and V, consecutive tokens on consecutive lanes.
+// Small writes (a decode or verify step): each thread quantizes 4 dimensions.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -81,18 +81,65 @@ __global__ __launch_bounds__(256) void kv_write_tokens_kernel(const WriteArgs a)
   for (int c = threadIdx.x >> 6; c < a.head_dim / 16; c += 4) write_chunk<ST, FMT>(a, t, blockIdx.y, c);
 }
 
-// Few tokens (a decode or verify step): one thread per 16-element chunk, all
-// chunks of all heads in flight at once.
+// Four dimensions [4q, 4q + 4) of token t, head h: 4 key codes (one store)
+// and 4 value codes (one per dimension row of the value group).
+template <int ST, int FMT>
+__device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int q) {
+  constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  const int64_t page = slot >> a.bs_log2;
+  const int off = (int)(slot & ((1 << a.bs_log2) - 1));
+  const int D = a.head_dim;
+  const int64_t src = ((int64_t)t * a.num_kv_heads + h) * D + 4 * q;
+  const int64_t ph = page * a.num_kv_heads + h;
+  uint8_t* kdst = a.key_cache + ((ph << a.bs_log2) + off) * D * ES + 4 * q * ES;
+  const int vg_log2 = a.bs_log2 < 6 ? a.bs_log2 : 6;
+  const int T = 1 << vg_log2;
+  uint8_t* vdst = a.value_cache +
+      ((((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D + 4 * q) * T + (off & (T - 1))) * ES;
+  const u32x2 kr = *reinterpret_cast<const u32x2*>(a.key + src);
+  const u32x2 vr = *reinterpret_cast<const u32x2*>(a.value + src);
+  if constexpr (FMT == KV_F16) {
+    *reinterpret_cast<u32x2*>(kdst) = kr;
+    uint16_t* vd = reinterpret_cast<uint16_t*>(vdst);
+    vd[0] = (uint16_t)vr.x;
+    vd[T] = (uint16_t)(vr.x >> 16);
+    vd[2 * T] = (uint16_t)vr.y;
+    vd[3 * T] = (uint16_t)(vr.y >> 16);
+  } else {
+    const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
+    const float kdiv = ksc ? a.k_scale[h] : 1.0f;
+    const float vdiv = vsc ? a.v_scale[h] : 1.0f;
+    const uint32_t kw[2] = {kr.x, kr.y}, vw[2] = {vr.x, vr.y};
+    uint32_t kout = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = src_to_f32<ST>((uint16_t)(kw[i >> 1] >> ((i & 1) * 16)));
+      const float y = ksc ? x / kdiv : x;   // IEEE fp32 division (correctly rounded)
+      kout |= (FMT == KV_E4M3 ? f32_to_e4m3(y) : f32_to_e5m2(y)) << (i * 8);
+    }
+    *reinterpret_cast<uint32_t*>(kdst) = kout;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = src_to_f32<ST>((uint16_t)(vw[i >> 1] >> ((i & 1) * 16)));
+      const float y = vsc ? x / vdiv : x;
+      vdst[i * T] = (uint8_t)(FMT == KV_E4M3 ? f32_to_e4m3(y) : f32_to_e5m2(y));
+    }
+  }
+}
+
+// Few tokens (a decode or verify step): one thread per four dimensions of one
+// token and head, so all of a step's conversions run side by side.
 template <int ST, int FMT>
 __global__ __launch_bounds__(256) void kv_write_chunks_kernel(const WriteArgs a) {
-  const int nc = a.head_dim / 16;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = a.num_tokens * a.num_kv_heads * nc;
-  if (id >= total) return;
-  const int c = (int)(id % nc);
-  const int h = (int)((id / nc) % a.num_kv_heads);
-  const int64_t t = id / ((int64_t)nc * a.num_kv_heads);
-  write_chunk<ST, FMT>(a, t, h, c);
+  const int nq = a.head_dim / 4;
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  const int per_token = nq * a.num_kv_heads;
+  if (id >= (int)a.num_tokens * per_token) return;
+  const int t = id / per_token;
+  const int r = id - t * per_token;
+  write_quad<ST, FMT>(a, t, r / nq, r % nq);
 }
 
 constexpr int64_t kFewTokens = 64;
@@ -100,7 +147,7 @@ constexpr int64_t kFewTokens = 64;
 template <int ST, int FMT>
 static void launch_write(const WriteArgs& a, hipStream_t s) {
   if (a.num_tokens < kFewTokens) {
-    const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 16);
+    const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
     hipLaunchKernelGGL((kv_write_chunks_kernel<ST, FMT>), dim3((unsigned)((total + 255) / 256)),
                        dim3(256), 0, s, a);
   } else {

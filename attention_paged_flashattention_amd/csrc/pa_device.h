@@ -107,34 +107,37 @@ __device__ __forceinline__ constexpr float kv_fold() {
 // ---------------------------------------------------------------------------
 // fp32 -> FP8, saturating, round to nearest even. Integer rounding of the
 // fp32 bit pattern for normals; rint of an exact power-of-two rescale in the
-// subnormal range. The sign bit is always kept.
+// subnormal range. The sign bit is always kept. Every case is computed and
+// the result picked by selects, so a wave never branches per element.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-  uint32_t u = __builtin_bit_cast(uint32_t, y);
-  uint32_t s = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return s | 0x7Fu;            // NaN
-  if (a >= 0x43E00000u) return s | 0x7Eu;           // >= 448 (and inf): saturate
-  if (a < 0x3C800000u) {                            // < 2^-6: quantum 2^-9
-    float f = __builtin_bit_cast(float, a) * 512.0f;
-    return s | (uint32_t)__builtin_rintf(f);        // 0..8 (8 = smallest normal)
-  }
-  uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);     // RNE to 3 mantissa bits
-  return s | ((r >> 20) - (120u << 3));
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  // below 2^-6 the quantum is 2^-9: rint(|y| * 512) in 0..8 (8 = smallest normal)
+  const float f = __builtin_bit_cast(float, a < 0x3C800000u ? a : 0x3C800000u) * 512.0f;
+  const uint32_t sub = (uint32_t)__builtin_rintf(f);
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);   // RNE to 3 mantissa bits
+  const uint32_t nrm = (r >> 20) - (120u << 3);
+  uint32_t c = a < 0x3C800000u ? sub : nrm;
+  c = a >= 0x43E00000u ? 0x7Eu : c;                      // >= 448 (and inf): saturate
+  c = a > 0x7F800000u ? 0x7Fu : c;                       // NaN
+  return s | c;
 }
 
 __device__ __forceinline__ uint32_t f32_to_e5m2(float y) {
-  uint32_t u = __builtin_bit_cast(uint32_t, y);
-  uint32_t s = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return s | 0x7Fu;            // NaN
-  if (a >= 0x47600000u) return s | 0x7Bu;           // >= 57344 (and inf): saturate
-  if (a < 0x38800000u) {                            // < 2^-14: quantum 2^-16
-    float f = __builtin_bit_cast(float, a) * 65536.0f;
-    return s | (uint32_t)__builtin_rintf(f);        // 0..4
-  }
-  uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);     // RNE to 2 mantissa bits
-  return s | ((r >> 21) - (112u << 2));
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  // below 2^-14 the quantum is 2^-16: rint(|y| * 65536) in 0..4
+  const float f = __builtin_bit_cast(float, a < 0x38800000u ? a : 0x38800000u) * 65536.0f;
+  const uint32_t sub = (uint32_t)__builtin_rintf(f);
+  const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);   // RNE to 2 mantissa bits
+  const uint32_t nrm = (r >> 21) - (112u << 2);
+  uint32_t c = a < 0x38800000u ? sub : nrm;
+  c = a >= 0x47600000u ? 0x7Bu : c;                      // >= 57344 (and inf): saturate
+  c = a > 0x7F800000u ? 0x7Fu : c;                       // NaN
+  return s | c;
 }
 
 // 16-bit source element -> fp32 (exact).
