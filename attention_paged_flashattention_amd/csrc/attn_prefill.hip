@@ -15,7 +15,7 @@
 //   K/V of one head while all its work-groups stream it. Query tiles with the
 //   most keys are dispatched first.
 // * Keys are walked in 64-key tiles. The 512 threads load the FP8 tile with
-//   128-bit loads (page id per 16-key run), dequantize in registers and store
+//   128-bit loads (one page id per tile), dequantize in registers and store
 //   16-bit K (token-major) and V (dimension-major) tiles in LDS, three
 //   buffers deep; loads run three tiles ahead of the tile being multiplied.
 // * Ping-pong: waves 0-3 and 4-7 share the SIMDs and cross the same two
@@ -110,6 +110,8 @@ void prefill_kernel(const PrefillArgs a) {
   const int bs_mask = (1 << bs_log2) - 1;
   const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
   const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
+  const __attribute__((address_space(4))) int32_t* btb_s =
+      (const __attribute__((address_space(4))) int32_t*)btb;
   const int64_t kvh = Hkv;
 
   const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
@@ -130,7 +132,12 @@ void prefill_kernel(const PrefillArgs a) {
   // ---- global -> register staging (all 512 threads) ----
   // K: thread owns key kt, dims kd0 .. kd0 + EPT - 1.
   // V: thread owns dim vd, keys vk0 .. vk0 + EPT - 1.
-  // Keys past the context are not loaded (zeros), so no stale slot -- NaN
+  // Every staging thread issues the same loads for every tile, whatever the
+  // context length: addresses of keys past the context are redirected to the
+  // tile's first key (tiles past the last one reload the last tile), and the
+  // data of such keys is zeroed when the tile is written to LDS. Loads that
+  // never depend on a branch let the compiler wait only for the tile being
+  // written, not for the loads issued since, and no stale slot -- NaN
   // included -- reaches the tiles.
   const int kt = tid / TPK, kd0 = (tid % TPK) * EPT;
   const int vd = tid / TPR, vk0 = (tid % TPR) * EPT;
@@ -142,48 +149,76 @@ void prefill_kernel(const PrefillArgs a) {
     u32x4 k[KLD], v[VLD];
   };
   const bool uni = bs_log2 >= 6;          // a 64-key tile lies in one page
+  const bool any_key = ctx > 0;           // else every load reads page 0 (discarded)
+  const int last_t0 = (ntiles - 1) * BN;
+
+  // Pages of >= 64 keys: a tile lies in one page, so its K and V sit at a
+  // uniform base (scalar arithmetic on the page id) plus per-thread offsets
+  // fixed for the whole loop; a key past the context reads the tile's first
+  // key instead.
+  const uint32_t koff = (uint32_t)((kt * D + kd0) * ES), koff0 = (uint32_t)(kd0 * ES);
+  const uint32_t voff0 = (uint32_t)((vd << 6) * ES);
 
   auto load_kv = [&](Stage& R, int t0) __attribute__((always_inline)) {
-    if (!stager) return;
-    // one uniform page-id load per tile when pages hold >= 64 keys
-    const int64_t tpage = uni ? (int64_t)btb[t0 >> bs_log2] : 0;
-    const int key = t0 + kt;
-    if (key < ctx) {
-      const int64_t page = uni ? tpage : (int64_t)btb[key >> bs_log2];
+    if constexpr (NSTAGE < NT) {
+      if (!stager) return;
+    }
+    t0 = __builtin_amdgcn_readfirstlane(min(t0, last_t0));
+    if (uni) {
+      // one page-id load per tile, scalar (block tables are read-only here):
+      // the vector-load counter does not track it, so waiting for it never
+      // waits for K/V loads in flight
+      const int64_t pg = (any_key ? (int64_t)btb_s[t0 >> bs_log2] : 0) * kvh + g;
+      const int toff = t0 & bs_mask;
+      const uint8_t* kb = a.key_cache + ((pg << bs_log2) + toff) * (int64_t)(D * ES);
+      const uint8_t* vb = a.value_cache + (((pg << (bs_log2 - 6)) + (toff >> 6)) * D << 6) * (int64_t)ES;
+      const uint32_t ko = t0 + kt < ctx ? koff : koff0;
+#pragma unroll
+      for (int x = 0; x < KLD; ++x) R.k[x] = ld16(kb + ko + 16 * x);
+#pragma unroll
+      for (int x = 0; x < VLD; ++x) {
+        const uint32_t vo = t0 + vk0 + x * KPL < ctx ? voff0 + (uint32_t)((vk0 + x * KPL) * ES) : voff0;
+        R.v[x] = ld16(vb + vo);
+      }
+    } else {
+      const int key = t0 + kt < ctx ? t0 + kt : t0;
+      const int64_t kpage = any_key ? (int64_t)btb[key >> bs_log2] : 0;
       const uint8_t* kp = a.key_cache +
-          (((page * kvh + g) << bs_log2) + (key & bs_mask)) * (int64_t)(D * ES) + kd0 * ES;
+          (((kpage * kvh + g) << bs_log2) + (key & bs_mask)) * (int64_t)(D * ES) + kd0 * ES;
 #pragma unroll
       for (int x = 0; x < KLD; ++x) R.k[x] = ld16(kp + 16 * x);
-    } else {
 #pragma unroll
-      for (int x = 0; x < KLD; ++x) R.k[x] = u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int x = 0; x < VLD; ++x) {
-      const int k0 = t0 + vk0 + x * KPL;
-      if (k0 < ctx) {
-        const int64_t page = uni ? tpage : (int64_t)btb[k0 >> bs_log2];
+      for (int x = 0; x < VLD; ++x) {
+        const int k0 = t0 + vk0 + x * KPL < ctx ? t0 + vk0 + x * KPL : t0;
+        const int64_t page = any_key ? (int64_t)btb[k0 >> bs_log2] : 0;
         const int vo = k0 & bs_mask;  // values: dimension-major inside 2^vg_log2-token groups
         const uint8_t* vp = a.value_cache +
             (((((page * kvh + g) << (bs_log2 - vg_log2)) + (vo >> vg_log2)) * D + vd) << vg_log2 |
              (vo & ((1 << vg_log2) - 1))) * (int64_t)ES;
-        u32x4 v = ld16(vp);
-        const int nvalid = ctx - k0;
-        if (nvalid < KPL) {
-          uint32_t e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < KPL; ++i) {
-            if (i >= nvalid) {
-              if constexpr (ES == 1) e[i >> 2] &= ~(0xFFu << ((i & 3) * 8));
-              else e[i >> 1] &= ~(0xFFFFu << ((i & 1) * 16));
-            }
-          }
-          v = u32x4{e[0], e[1], e[2], e[3]};
-        }
-        R.v[x] = v;
-      } else {
-        R.v[x] = u32x4{0, 0, 0, 0};
+        R.v[x] = ld16(vp);
       }
+    }
+  };
+
+  // Keys at or past the context are zeroed here: K rows whole, V runs from
+  // the first such key on (selects on the raw words, no branch).
+  auto mask_kv = [&](Stage& R, int t0) __attribute__((always_inline)) {
+    const uint32_t kmask = t0 + kt < ctx ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int x = 0; x < KLD; ++x) R.k[x] &= kmask;
+#pragma unroll
+    for (int x = 0; x < VLD; ++x) {
+      const int nvalid = ctx - (t0 + vk0 + x * KPL);   // valid keys in this 16-byte run
+      uint32_t wm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int per = 4 / ES;                        // keys per 32-bit word
+        const int nv = nvalid - i * per;
+        const uint32_t part = ES == 1 ? (1u << (8 * (nv > 0 ? nv : 0) & 31)) - 1u
+                                      : (nv > 0 ? 0x0000FFFFu : 0u);
+        wm[i] = nv >= per ? 0xFFFFFFFFu : (nv <= 0 ? 0u : part);
+      }
+      R.v[x] &= u32x4{wm[0], wm[1], wm[2], wm[3]};
     }
   };
 
@@ -191,8 +226,11 @@ void prefill_kernel(const PrefillArgs a) {
   // inverse), so the MFMA operand read of row R is unpermuted and consecutive
   // lanes hit consecutive rows.
   const int kt_row = (kt & ~31) | kappa(kt & 31);
-  auto store_kv = [&](const Stage& R, int buf) __attribute__((always_inline)) {
-    if (!stager) return;
+  auto store_kv = [&](Stage R, int buf, int t0) __attribute__((always_inline)) {
+    if constexpr (NSTAGE < NT) {
+      if (!stager) return;
+    }
+    if (t0 + BN > ctx) mask_kv(R, t0);   // only the tile that crosses the context end
     uint16_t* kdst = &sk[buf][kt_row * KPAD + kd0];
     uint16_t* vdst = &sv[buf][vd * VPAD + vk0];
     if constexpr (FMT == KV_F16) {
@@ -269,7 +307,7 @@ void prefill_kernel(const PrefillArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sacc[mb][j]);
-    tm = fmaxf(tm, lane_xor(tm, 32));
+    tm = half_swap_max(tm);
     // Lazy rescaling: O and l are kept relative to a running max m that is
     // raised only when some row of the wave sees a max larger than m + 8
     // (log2 units). p = 2^(s*C - m) then stays <= 2^8 (fine in fp16), and O/l
@@ -283,16 +321,29 @@ void prefill_kernel(const PrefillArgs a) {
       for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
     }
     const float muse = m == kNegInfP ? 0.0f : m;
-    float ps = 0.0f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][j], C, -muse));
-        ps += pv;
         pop[mb * 2 + (j >> 3)][j & 7] = (_Float16)pv;
       }
-    l += ps;
+    // the row sum adds the fp16 P that the PV product uses, two per dot2
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // (vector elements are copied to scalars before the bit casts: this
+      // compiler reads element 0 when a bit cast takes a vector element)
+      const u32x4 w = __builtin_bit_cast(u32x4, pop[i]);
+      const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+      ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w0), one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w1), one, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w2), one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w3), one, ps1, false);
+    }
+    l += ps0 + ps1;
   };
 
   // O^T += V^T P^T with V from buffer vb, operands read PF ahead.
@@ -327,18 +378,16 @@ void prefill_kernel(const PrefillArgs a) {
   // last reader (B's PV of tile n-1).
   Stage R0, R1;
   load_kv(R0, 0);
-  store_kv(R0, 0);
-  if (ntiles > 1) {
-    load_kv(R1, BN);
-    store_kv(R1, 1);
-  }
-  if (ntiles > 2) load_kv(R0, 2 * BN);
+  store_kv(R0, 0, 0);
+  load_kv(R1, BN);
+  if (ntiles > 1) store_kv(R1, 1, BN);
+  load_kv(R0, 2 * BN);
   __syncthreads();
   if (!grp_b) qk(0);
   __syncthreads();
   // Rl receives tile n+3, Rs holds tile n+2.
   auto iteration = [&](int n, Stage& Rl, const Stage& Rs) __attribute__((always_inline)) {
-    if (n + 3 < ntiles) load_kv(Rl, (n + 3) * BN);
+    load_kv(Rl, (n + 3) * BN);
     // phase 1
     if (!grp_b) {
       softmax(n * BN);
@@ -348,7 +397,7 @@ void prefill_kernel(const PrefillArgs a) {
     }
     __syncthreads();
     // phase 2
-    if (n + 2 < ntiles) store_kv(Rs, (n + 2) % NBUF);
+    if (n + 2 < ntiles) store_kv(Rs, (n + 2) % NBUF, (n + 2) * BN);
     if (!grp_b) {
       pv(n % NBUF);
       if (n + 1 < ntiles) qk((n + 1) % NBUF);
@@ -357,14 +406,17 @@ void prefill_kernel(const PrefillArgs a) {
     }
     __syncthreads();
   };
-  for (int n = 0; n < ntiles; n += 2) {
+  // pairs of tiles, so the loop body always issues the same loads
+  int n = 0;
+  for (; n + 1 < ntiles; n += 2) {
     iteration(n, R1, R0);
-    if (n + 1 < ntiles) iteration(n + 1, R0, R1);
+    iteration(n + 1, R0, R1);
   }
+  if (n < ntiles) iteration(n, R1, R0);
   if (grp_b) pv((ntiles - 1) % NBUF);
 
   // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r].
-  l += lane_xor(l, 32);
+  l = half_swap_sum(l);
   if (!rvalid) return;
   const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
   const float f = l > 0.0f ? vscale / l : 0.0f;
