@@ -24,7 +24,7 @@
 //   of the PV MFMA is one 128-bit load, no transpose) and a tile's values are
 //   one contiguous 8 KiB run, like its keys.
 // * Online softmax per row in exp2 units; the row max is reduced across the 4
-//   lanes that share a row with two cross-lane exchanges, the row sum stays
+//   lanes that share a row with two lane-swap instructions, the row sum stays
 //   lane-partial until the end.
 // * The 4 waves' (m, l, O) are merged through LDS, and each work-group writes
 //   one partial per row; the combine kernel merges the partitions in a fixed
@@ -284,8 +284,7 @@ void decode_split_kernel(const DecodeArgs a) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sacc[nb][s][i]);
-      tm = fmaxf(tm, lane_xor(tm, 16));
-      tm = fmaxf(tm, lane_xor(tm, 32));
+      tm = swap_max<32>(swap_max<16>(tm));
       // Lazy rescaling (see the prefill kernel): the reference max is raised
       // only when some row's max exceeds it by more than 2^8.
       const float mcand = fmaxf(m[nb], tm * C);
@@ -355,8 +354,7 @@ void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     float lf = l[nb];
-    lf += lane_xor(lf, 16);
-    lf += lane_xor(lf, 32);
+    lf = swap_sum<32>(swap_sum<16>(lf));
     if (qg == 0) {
       sm_m[w][c] = m[nb];
       sm_l[w][c] = lf;

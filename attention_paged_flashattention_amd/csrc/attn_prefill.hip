@@ -307,7 +307,7 @@ void prefill_kernel(const PrefillArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sacc[mb][j]);
-    tm = half_swap_max(tm);
+    tm = swap_max<32>(tm);
     // Lazy rescaling: O and l are kept relative to a running max m that is
     // raised only when some row of the wave sees a max larger than m + 8
     // (log2 units). p = 2^(s*C - m) then stays <= 2^8 (fine in fp16), and O/l
@@ -416,7 +416,7 @@ void prefill_kernel(const PrefillArgs a) {
   if (grp_b) pv((ntiles - 1) % NBUF);
 
   // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r].
-  l = half_swap_sum(l);
+  l = swap_sum<32>(l);
   if (!rvalid) return;
   const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
   const float f = l > 0.0f ? vscale / l : 0.0f;

@@ -178,24 +178,40 @@ __device__ __forceinline__ float lane_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
-// Cross-half reductions of a wave64 (lanes l and l ^ 32): one
-// v_permlane32_swap, no LDS round trip. With the same value in both operands
-// the swap leaves the lower half's values in every lane of one output and the
-// upper half's in every lane of the other, so combining the two outputs with
-// a symmetric operation reduces each lane with its partner. (The outputs are
-// copied to scalars before the bit casts: this compiler reads element 0 when
-// a bit cast takes a vector element.)
-__device__ __forceinline__ float half_swap_max(float v) {
+// Reductions between lanes l and l ^ 32 (permlane32 swap) or l and l ^ 16
+// (permlane16 swap) of a wave64: one VALU instruction, no LDS round trip.
+// With the same value in both operands, a swap leaves one member of each lane
+// pair's values in one output and the other member's in the other output, so
+// combining the two outputs with a symmetric operation reduces each lane with
+// its partner. (The outputs are copied to scalars before the bit casts: this
+// compiler reads element 0 when a bit cast takes a vector element.)
+template <int XOR>
+__device__ __forceinline__ float swap_max(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const uint32_t r0 = r[0], r1 = r[1];
+  uint32_t r0, r1;
+  if constexpr (XOR == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = r[0]; r1 = r[1];
+  } else {
+    static_assert(XOR == 16, "lane distance 16 or 32");
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = r[0]; r1 = r[1];
+  }
   return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 
-__device__ __forceinline__ float half_swap_sum(float v) {
+template <int XOR>
+__device__ __forceinline__ float swap_sum(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const uint32_t r0 = r[0], r1 = r[1];
+  uint32_t r0, r1;
+  if constexpr (XOR == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = r[0]; r1 = r[1];
+  } else {
+    static_assert(XOR == 16, "lane distance 16 or 32");
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = r[0]; r1 = r[1];
+  }
   return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 

@@ -249,6 +249,33 @@ def headline_decode_128k(seed=1006, ctx=131072, partitions=64):
                      meta=dict(partitions=partitions))
 
 
+# --------------------------------------------------------------------------
+# Second workloads on the same kernels (seeds 1007..1009).
+# --------------------------------------------------------------------------
+
+def batched_decode_e5m2_16k(seed=1007, batch=16, ctx=16384):
+    """16 sequences at 16384 tokens each, decode (one query each). Hq=32,
+    Hkv=8, D=128, fp16 Q/K/V ~ N(0,1), E5M2 KV (no scales), 16-token pages,
+    random page permutation."""
+    return make_case("decode_b16_16k_e5m2_bs16", seed, [ctx] * batch, 1, 32, 8, 128, 16,
+                     "f16", "f16", "e5m2")
+
+
+def verify_q16_128k(seed=1008, ctx=131072):
+    """The q8 verify recipe with 16 new causal queries per sequence (the
+    wider lookup verification): 4 sequences at 131072 tokens (queries at
+    131056..131071), E5M2 KV, K/V ~ N(0, 0.5), 2048-token pages."""
+    return make_case("verify_q16_b4_128k_e5m2_bs2048", seed, [ctx] * 4, 16, 32, 8, 128,
+                     2048, "f16", "f16", "e5m2", sigma_kv=0.5)
+
+
+def chunked_prefill_64k(seed=1009, total=65536, chunk=4096):
+    """The 32K chunked-prefill recipe to 65536 tokens (32 pages of 2048);
+    run in 4096- or 8192-token chunks."""
+    return make_case(f"prefill64k_chunk{chunk // 1024}k_bf16_e4m3_bs2048", seed, [total], [total],
+                     32, 8, 128, 2048, "bf16", "bf16", "e4m3", meta=dict(chunk=chunk))
+
+
 WORKLOADS = {
     1: prefill_decode_small,
     2: batched_decode_e4m3,
@@ -256,4 +283,7 @@ WORKLOADS = {
     4: verify_q8_128k,
     5: long_decode_256k,
     "H": headline_decode_128k,
+    "b16": batched_decode_e5m2_16k,
+    "q16": verify_q16_128k,
+    "64k": chunked_prefill_64k,
 }

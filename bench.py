@@ -11,14 +11,17 @@ log-sum-exp combine -- every step of the decode path. Four copies of the 256 MiB
 cache are used in rotation so that no step finds its cache in the 256 MB
 last-level cache. The same line carries the 32K chunked-prefill throughput
 (useful causal TFLOP/s; one step = 8 chunks of 4096 tokens, each a write then a
-prefill), the q8 verify at 128K, the 256K decode and the batched decode, the
-roofline of the dominant kernels, and the CPU oracle timed on a bounded
-sample of the headline workload.
+prefill), the q8 and q16 verify at 128K, the 256K decode, the batched decodes
+(8 x 1K-4K E4M3, 16 x 16K E5M2), the 64K prefill in 4096- and 8192-token
+chunks, the write kernel's rate, the small prefill+decode workload's latency,
+the cost of a decode call with nothing to read, the roofline of the dominant
+kernels, and the CPU oracle timed on a bounded sample of the headline
+workload.
 
 Each section times its steps twice: a plain loop gives the step rate, and a
 second loop of the same steps, with timing-only HIP events recorded by the
 library around every launch of the dominant kernel on its stream, gives that
-kernel's average launch duration.
+kernel's launch durations (average, and 10th/50th/90th percentiles).
 
 Inputs are synthetic and seeded (attention_paged_flashattention_amd.synth) and
 already resident in HBM when a timed region starts.
@@ -38,7 +41,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS_16 = 2500.0    # MI355X dense fp16 / bf16 MFMA
 METRIC = "paged-attn decode GB/s (%HBM peak) @128K FP8 KV; prefill TFLOP/s @32K"
-SECTIONS = ["decode128k", "prefill32k", "verify128k", "decode256k", "decode_b8", "copy"]
+SECTIONS = ["decode128k", "prefill32k", "verify128k", "verify_q16", "decode256k", "decode_b8",
+            "decode_b16", "prefill64k", "small", "empty", "copy"]
 
 
 def log(msg):
@@ -68,6 +72,11 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed: {rc}")
         return ev.value
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -115,6 +124,12 @@ def timed(fn, steps, warmup):
         fn(i, True)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def pct(v, q):
+    """q-th percentile (nearest rank) of a list."""
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
 
 
 def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
@@ -177,6 +192,8 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
     torch.cuda.empty_cache()
     return dict(name=name, ms_per_step=ms, ms_per_step_with_events=ms_ev, step_bytes=step_bytes,
                 GBps=step_bytes / ms / 1e6,
+                split_us_p10=pct(kern, 10) * 1e3, split_us_p50=pct(kern, 50) * 1e3,
+                split_us_p90=pct(kern, 90) * 1e3,
                 split_ms=kern_ms, split_bytes=split_bytes,
                 split_GBps=split_bytes / kern_ms / 1e6,
                 partitions=pa.pa_decode_partitions(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
@@ -187,15 +204,17 @@ def dc_max(c):
     return int(max(int(x) for x in c.ctx_lens))
 
 
-def prefill_section(ev, steps, warmup):
+def prefill_section(ev, case, steps, warmup, time_writes=False):
+    """Chunked prefill of one sequence: each step writes chunk c's K/V and
+    runs its prefill against the paged prefix (ctx = chunk (c + 1))."""
     import torch
     from attention_paged_flashattention_amd import pagedattn as pa
-    from attention_paged_flashattention_amd import runner, synth
+    from attention_paged_flashattention_amd import runner
 
-    case = synth.chunked_prefill_32k()
     dc = runner.DeviceCase(case)
     chunk = case.meta["chunk"]
-    n = 32768 // chunk
+    total = int(case.ctx_lens[0])
+    n = total // chunk
     dev = dc.device
     cu = torch.tensor([0, chunk], dtype=torch.int32, device=dev)
     ctxs = [torch.tensor([chunk * (i + 1)], dtype=torch.int32, device=dev) for i in range(n)]
@@ -227,14 +246,113 @@ def prefill_section(ev, steps, warmup):
     D, Hq = case.head_dim, case.num_q_heads
     chunk_flops = [4 * D * Hq * (chunk * chunk * ci + chunk * (chunk + 1) // 2) for ci in range(n)]
     flops = sum(chunk_flops)
-    kern_ms = sum(sum(x) for x in per_chunk) / steps
+    step_kern = [sum(x) for x in per_chunk]
+    kern_ms = sum(step_kern) / steps
     last_ms = sum(x[-1] for x in per_chunk) / steps
+    res = dict(name=case.name, chunk=chunk, ms_per_step=ms, flops=flops, TFLOPs=flops / ms / 1e9,
+               kernel_ms=kern_ms, kernel_TFLOPs=flops / kern_ms / 1e9,
+               kernel_ms_p10=pct(step_kern, 10), kernel_ms_p50=pct(step_kern, 50),
+               kernel_ms_p90=pct(step_kern, 90),
+               last_chunk_ms=last_ms, last_chunk_TFLOPs=chunk_flops[-1] / last_ms / 1e9,
+               launches_per_step=n)
+    if time_writes:
+        # the write kernel alone: every chunk's write again (same bytes), events
+        # around each launch
+        ws = [[ev.create() for _ in range(n)] for _ in range(steps)]
+        we = [[ev.create() for _ in range(n)] for _ in range(steps)]
+
+        def wstep(i, record):
+            for ci in range(n):
+                if record:
+                    pa.pa_profile_next_call(ws[i][ci], we[i][ci])
+                writes[ci]()
+
+        timed(wstep, steps, 1)
+        wt = [ev.elapsed_ms(a, b) for sa, so in zip(ws, we) for a, b in zip(sa, so)]
+        src_bytes = 2 if case.kv_dtype in ("f16", "bf16") else 4
+        cache_bytes = 2 if case.cache_fmt == "f16" else 1
+        per_tok = case.num_kv_heads * case.head_dim * 2 * (src_bytes + cache_bytes) + 8
+        wbytes = chunk * per_tok + (0 if case.k_scale is None else 2 * case.num_kv_heads * 4)
+        wavg = sum(wt) / len(wt)
+        res.update(write_bytes_per_launch=wbytes, write_us=wavg * 1e3,
+                   write_GBps=wbytes / wavg / 1e6)
     del dc
     torch.cuda.empty_cache()
-    return dict(ms_per_step=ms, flops=flops, TFLOPs=flops / ms / 1e9,
-                kernel_ms=kern_ms, kernel_TFLOPs=flops / kern_ms / 1e9,
-                last_chunk_ms=last_ms, last_chunk_TFLOPs=chunk_flops[-1] / last_ms / 1e9,
-                launches_per_step=n)
+    return res
+
+
+def small_section(ev, steps):
+    """The small workload: prefill of 64 tokens (Hq 4, Hkv 1, D 64, fp16
+    cache, 16-token pages) and the decode at position 64; latency of each
+    call pair (write + attention), events around the pair on the stream."""
+    import torch
+    from attention_paged_flashattention_amd import pagedattn as pa
+    from attention_paged_flashattention_amd import runner, synth
+
+    case = synth.prefill_decode_small()
+    dc = runner.DeviceCase(case)
+    dev = dc.device
+    cu = torch.tensor([0, 64], dtype=torch.int32, device=dev)
+    ctx64 = torch.tensor([64], dtype=torch.int32, device=dev)
+    ctx65 = torch.tensor([65], dtype=torch.int32, device=dev)
+    wpf = pa.bind_kv_cache_write_fp8(dc.k[:64], dc.v[:64], dc.slots[:64], dc.key_cache,
+                                     dc.value_cache, "f16")
+    pf = pa.bind_attn_prefill_paged(dc.q[:64], cu, 64, dc.key_cache, dc.value_cache, "f16",
+                                    dc.block_tables, ctx64, 64, case.softmax_scale)[0]
+    wdec = pa.bind_kv_cache_write_fp8(dc.k[64:65], dc.v[64:65], dc.slots[64:65], dc.key_cache,
+                                      dc.value_cache, "f16")
+    qd = dc.q[64:65].contiguous()
+    dec = pa.bind_attn_decode_paged(qd, dc.key_cache, dc.value_cache, "f16", dc.block_tables,
+                                    ctx65, 65, case.softmax_scale)[0]
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, calls in (("prefill64_us", (wpf, pf)), ("decode_at_64_us", (wdec, dec))):
+        evs = [(ev.create(), ev.create()) for _ in range(steps)]
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        for a, b in evs:
+            ev.record(a, stream)
+            for c in calls:
+                c()
+            ev.record(b, stream)
+        torch.cuda.synchronize()
+        t = [ev.elapsed_ms(a, b) * 1e3 for a, b in evs]
+        res[name] = round(pct(t, 50), 2)
+    del dc
+    torch.cuda.empty_cache()
+    return res
+
+
+def empty_section(ev, steps):
+    """A decode call of the 128K headline shape whose context is empty: the
+    grid is launched and every work-group finds nothing to read. Its time is
+    the fixed cost of the two launches (split + combine), events around the
+    call on the stream."""
+    import torch
+    from attention_paged_flashattention_amd import pagedattn as pa
+
+    dev = "cuda:0"
+    nb, hkv, bs, d, hq = 8, 8, 2048, 128, 32
+    kc = torch.zeros((nb, hkv, bs, d), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((nb, hkv, bs // 64, d, 64), dtype=torch.uint8, device=dev)
+    bt = torch.zeros((1, 64), dtype=torch.int32, device=dev)
+    ctx = torch.zeros((1,), dtype=torch.int32, device=dev)
+    sc = torch.ones((hkv,), dtype=torch.float32, device=dev)
+    q = torch.zeros((1, hq, d), dtype=torch.float16, device=dev)
+    call = pa.bind_attn_decode_paged(q, kc, vc, "e4m3", bt, ctx, 131072, 0.0884, sc, sc,
+                                     num_partitions=64)[0]
+    stream = torch.cuda.current_stream().cuda_stream
+    call()
+    torch.cuda.synchronize()
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
+    for a, b in evs:
+        ev.record(a, stream)
+        call()
+        ev.record(b, stream)
+    torch.cuda.synchronize()
+    t = [ev.elapsed_ms(a, b) * 1e3 for a, b in evs]
+    return dict(decode_call_us=round(pct(t, 50), 2))
 
 
 def copy_section(ev, steps):
@@ -319,7 +437,7 @@ def _cpu_baseline(seconds_target):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sections", default=",".join(SECTIONS),
                     help="comma-separated subset of " + ",".join(SECTIONS))
@@ -356,11 +474,16 @@ def main():
                                                 "decode_128k_e4m3_bs2048_p64")
     if "prefill32k" in sections:
         log("section prefill32k")
-        res["prefill32k"] = prefill_section(ev, max(2, K // 5), max(1, W // 5))
+        res["prefill32k"] = prefill_section(ev, synth.chunked_prefill_32k(), max(10, K // 5),
+                                            max(1, W // 5), time_writes=True)
     if "verify128k" in sections:
         log("section verify128k")
         res["verify128k"] = decode_like_section(ev, synth.verify_q8_128k(), K, W, 1, 8,
                                                 "verify_q8_b4_128k_e5m2_bs2048")
+    if "verify_q16" in sections:
+        log("section verify_q16")
+        res["verify_q16"] = decode_like_section(ev, synth.verify_q16_128k(), K, W, 1, 16,
+                                                "verify_q16_b4_128k_e5m2_bs2048")
     if "decode256k" in sections:
         log("section decode256k")
         res["decode256k"] = decode_like_section(ev, synth.long_decode_256k(), K, W, 1, 1,
@@ -369,6 +492,21 @@ def main():
         log("section decode_b8")
         res["decode_b8"] = decode_like_section(ev, synth.batched_decode_e4m3(), K, W, 8, 1,
                                                "decode_b8_1k4k_e4m3_bs16")
+    if "decode_b16" in sections:
+        log("section decode_b16")
+        res["decode_b16"] = decode_like_section(ev, synth.batched_decode_e5m2_16k(), K, W, 2, 1,
+                                                "decode_b16_16k_e5m2_bs16")
+    if "prefill64k" in sections:
+        for chunk in (4096, 8192):
+            log(f"section prefill64k chunk {chunk}")
+            res[f"prefill64k_{chunk}"] = prefill_section(ev, synth.chunked_prefill_64k(chunk=chunk),
+                                                         max(5, K // 10), 1)
+    if "small" in sections:
+        log("section small")
+        res["small"] = small_section(ev, K)
+    if "empty" in sections:
+        log("section empty")
+        res["empty"] = empty_section(ev, K)
 
     cpu = None
     if not args.no_cpu_baseline and "decode128k" in sections:
@@ -394,7 +532,9 @@ def main():
                             "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": tr,
                             "algorithmic_bytes_per_launch": h["split_bytes"],
-                            "avg_launch_us": round(h["split_ms"] * 1e3, 2)}
+                            "avg_launch_us": round(h["split_ms"] * 1e3, 2),
+                            "p10_p50_p90_us": [round(h["split_us_p10"], 2), round(h["split_us_p50"], 2),
+                                               round(h["split_us_p90"], 2)]}
     else:
         line.update(value=None, unit="GB/s", ms_per_step=None, dtype="fp16", config={})
     p = res.get("prefill32k")
@@ -404,7 +544,14 @@ def main():
                                "frac_of_peak": round(p["TFLOPs"] / MFMA_PEAK_TFLOPS_16, 4),
                                "useful_causal_flops": p["flops"],
                                "last_chunk_TFLOPs": round(p["last_chunk_TFLOPs"], 1),
-                               "last_chunk_ms": round(p["last_chunk_ms"], 3), "dtype": "bf16"}
+                               "last_chunk_ms": round(p["last_chunk_ms"], 3), "dtype": "bf16",
+                               "kernel_ms_per_step_p10_p50_p90": [round(p["kernel_ms_p10"], 3),
+                                                                  round(p["kernel_ms_p50"], 3),
+                                                                  round(p["kernel_ms_p90"], 3)]}
+        line["write_kernel"] = {"workload": "4096-token chunk writes of the 32K prefill (bf16 -> E4M3)",
+                                "GBps": round(p["write_GBps"], 1), "us_per_launch": round(p["write_us"], 2),
+                                "bytes_per_launch": p["write_bytes_per_launch"],
+                                "frac_of_hbm_peak": round(p["write_GBps"] / HBM_PEAK_GBPS, 4)}
         trp = counters("prefill_32k_e4m3", pf_sha)
         line["roofline_prefill"] = {"bound": "mfma", "kernel": "prefill_kernel",
                                     "achieved": round(p["kernel_TFLOPs"], 1),
@@ -413,8 +560,9 @@ def main():
                                     "traffic": trp,
                                     "algorithmic_flops_per_step": p["flops"],
                                     "avg_launch_us": round(p["kernel_ms"] / p["launches_per_step"] * 1e3, 1)}
-    for key, out_key in [("verify128k", "verify_q8_128k"), ("decode256k", "decode_256k"),
-                         ("decode_b8", "decode_b8")]:
+    for key, out_key in [("verify128k", "verify_q8_128k"), ("verify_q16", "verify_q16_128k"),
+                         ("decode256k", "decode_256k"), ("decode_b8", "decode_b8"),
+                         ("decode_b16", "decode_b16_16k_e5m2")]:
         r = res.get(key)
         if r:
             line[out_key] = {"workload": r["name"], "GBps": round(r["GBps"], 1),
@@ -422,7 +570,25 @@ def main():
                              "frac_of_hbm_peak": round(r["GBps"] / HBM_PEAK_GBPS, 4),
                              "split_kernel_GBps": round(r["split_GBps"], 1),
                              "split_kernel_us": round(r["split_ms"] * 1e3, 2),
+                             "split_kernel_frac": round(r["split_GBps"] / HBM_PEAK_GBPS, 4),
+                             "split_us_p10_p50_p90": [round(r["split_us_p10"], 2),
+                                                      round(r["split_us_p50"], 2),
+                                                      round(r["split_us_p90"], 2)],
                              "partitions": r["partitions"]}
+    for chunk in (4096, 8192):
+        r = res.get(f"prefill64k_{chunk}")
+        if r:
+            line[f"prefill_64k_chunk{chunk // 1024}k"] = {
+                "workload": r["name"], "TFLOPs": round(r["TFLOPs"], 1),
+                "ms_per_step": round(r["ms_per_step"], 3),
+                "frac_of_peak": round(r["TFLOPs"] / MFMA_PEAK_TFLOPS_16, 4),
+                "kernel_TFLOPs": round(r["kernel_TFLOPs"], 1),
+                "last_chunk_TFLOPs": round(r["last_chunk_TFLOPs"], 1),
+                "launches_per_step": r["launches_per_step"]}
+    if "small" in res:
+        line["small_prefill64_decode_latency"] = dict(res["small"], workload="prefill64_decode_fp16_d64")
+    if "empty" in res:
+        line["empty_context_decode"] = dict(res["empty"], shape="128K headline launch, ctx 0")
     if "copy" in res:
         line["hbm_copy_GBps"] = round(res["copy"]["GBps"], 1)
     if cpu:

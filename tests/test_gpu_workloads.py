@@ -161,3 +161,62 @@ def test_headline_decode_128k(runner):
     a = dc.decode(num_partitions=case.meta["partitions"])
     torch.cuda.synchronize()
     assert torch.equal(out16, a)
+
+
+# ---------------------------------------------------------------------------
+# Second workloads on the same kernels
+# ---------------------------------------------------------------------------
+
+def test_batched_decode_e5m2_b16_16k(runner):
+    case = synth.batched_decode_e5m2_16k()
+    log(case.name)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.decode(out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _hull_check(out, dc)
+    _sampled_decode_check(case, dc, out, [(0, 0), (5, 2), (11, 7), (15, 4)])
+
+
+def test_verify_q16_128k(runner):
+    case = synth.verify_q16_128k()
+    log(case.name)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.verify(16, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _hull_check(out, dc)
+    _sampled_decode_check(case, dc, out, [(0, 2), (3, 6)])
+
+
+@pytest.mark.parametrize("chunk", [4096, 8192])
+def test_chunked_prefill_64k(runner, chunk):
+    """64K prefill in 16 chunks of 4096 or 8 of 8192; sampled rows of the
+    first, a middle and the last chunk against the oracle, every chunk for
+    the hull property."""
+    case = synth.chunked_prefill_64k(chunk=chunk)
+    log(case.name)
+    dc = runner.DeviceCase(case)
+    heads = np.array([3, 20])
+    kv_heads = sorted(set(int(h) // case.gqa for h in heads))
+    kc, vc = oracle_cache_heads(case, [(0, g) for g in kv_heads])
+    q32 = synth.to_f32(case.q, "bf16")
+    rng = np.random.default_rng(4)
+    n = 65536 // chunk
+    for c in range(n):
+        s, e = c * chunk, (c + 1) * chunk
+        out = dc.prefill_chunk(s, e, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _hull_check(out, dc)
+        if c not in (0, n // 2, n - 1):
+            continue
+        pos = np.unique(np.concatenate([[s, e - 1], rng.integers(s, e, size=4)]))
+        rows_q, rows_h, rows_p = [], [], []
+        for p in pos:
+            for h in heads:
+                rows_q.append(q32[p, h])
+                rows_h.append(h)
+                rows_p.append(p)
+        ref = oracle_rows(case, kc, vc, 0, np.array(rows_q), rows_h, rows_p)
+        got = out.cpu()[torch.tensor(np.array(rows_p) - s), torch.tensor(rows_h)]
+        check_close(got, ref, "e4m3", f"chunk {c} sampled rows")
