@@ -26,6 +26,19 @@ m = -inf, l = 0.
 definition; ``attend_partitioned`` exists only to self-test the log-sum-exp
 combine algebra.
 
+Sliding-window attention ("1Cat-vLLM 1.5.0" RELEASE notes, "Production
+DFlash2 on V100": the draft model's non-causal sliding-window attention;
+"Flash-V100 long-context improvements": that attention skips the prefix tiles
+outside the window). The pages give no formula; the reading taken is the usual
+one for a left window of ``W`` keys with no causal mask: query i of a block of
+``q_len`` sits at ``pos = ctx_b - q_len_b + i`` and attends every key j with
+
+    pos - W <= j < ctx_b
+
+-- the W keys before its own position, its own key, and every later key of
+its block. The arithmetic per row is the same as above over that key set;
+``W >= ctx_b`` gives plain non-causal attention over the whole context.
+
 Rows are processed a block at a time purely to bound memory; each row's
 arithmetic is the definition above.
 """
@@ -36,7 +49,14 @@ from . import paged
 
 
 def _rows_attend(qrows, pos, K, V, scale):
-    """qrows [R, D] float64, pos [R] int. Returns o [R, D], m [R], l [R], P [R, ctx]."""
+    """Causal rows: row r sees keys 0..pos[r]."""
+    pos = np.asarray(pos)
+    return _rows_attend_range(qrows, np.zeros_like(pos), pos, K, V, scale)
+
+
+def _rows_attend_range(qrows, lo, hi, K, V, scale):
+    """qrows [R, D] float64; row r sees keys lo[r]..hi[r] (inclusive) of the
+    ctx keys in K, V. Returns o [R, D], m [R], l [R], P [R, ctx]."""
     R, D = qrows.shape
     ctx = K.shape[0]
     o = np.zeros((R, D))
@@ -47,7 +67,7 @@ def _rows_attend(qrows, pos, K, V, scale):
         return o, m, l, P
     s = scale * (qrows @ K.T)                       # [R, ctx]
     j = np.arange(ctx)
-    visible = j[None, :] <= pos[:, None]
+    visible = (j[None, :] >= np.asarray(lo)[:, None]) & (j[None, :] <= np.asarray(hi)[:, None])
     has = visible.any(axis=1)
     s = np.where(visible, s, -np.inf)
     m_h = s[has].max(axis=1)
@@ -60,12 +80,23 @@ def _rows_attend(qrows, pos, K, V, scale):
     return o, m, l, P
 
 
+def _row_keys(pos, ctx, window):
+    """Visible key range (inclusive) of rows at positions pos: causal 0..pos,
+    or pos - window .. ctx - 1 for the non-causal sliding window."""
+    pos = np.asarray(pos)
+    if window is None:
+        return np.zeros_like(pos), pos
+    return pos - int(window), np.full_like(pos, ctx - 1)
+
+
 def attend(q, q_lens, ctx_lens, k_cache, v_cache, block_tables, fmt,
            num_kv_heads, softmax_scale, k_scale=None, v_scale=None,
-           return_probs=False, row_block=256):
+           return_probs=False, row_block=256, window=None):
     """q: [total_q, Hq, D] (sequences concatenated, seq b owns q_lens[b] rows).
     Returns o [total_q, Hq, D] float64, m and l [total_q, Hq]
-    (m in natural-log units), and the probabilities when asked (tiny inputs)."""
+    (m in natural-log units), and the probabilities when asked (tiny inputs).
+    ``window=None`` is causal attention; an integer W >= 0 is the non-causal
+    sliding window of W keys."""
     q = np.asarray(q)
     total_q, Hq, D = q.shape
     Hkv = int(num_kv_heads)
@@ -89,7 +120,11 @@ def attend(q, q_lens, ctx_lens, k_cache, v_cache, block_tables, fmt,
                     h = g * G + gh
                     rows = q[start + i0:start + i1, h, :].astype(np.float64)
                     pos = ctx - qlen + np.arange(i0, i1)
-                    ob, mb, lb, Pb = _rows_attend(rows, pos, K, V, scale)
+                    if window is None:
+                        ob, mb, lb, Pb = _rows_attend(rows, pos, K, V, scale)
+                    else:
+                        lo, hi = _row_keys(pos, ctx, window)
+                        ob, mb, lb, Pb = _rows_attend_range(rows, lo, hi, K, V, scale)
                     o[start + i0:start + i1, h] = ob
                     m[start + i0:start + i1, h] = mb
                     l[start + i0:start + i1, h] = lb
@@ -103,7 +138,8 @@ def attend(q, q_lens, ctx_lens, k_cache, v_cache, block_tables, fmt,
 
 
 def attend_rows(q_rows, heads, positions, seq_ctx, k_cache, v_cache, block_table,
-                fmt, num_q_heads, num_kv_heads, softmax_scale, k_scale=None, v_scale=None):
+                fmt, num_q_heads, num_kv_heads, softmax_scale, k_scale=None, v_scale=None,
+                window=None):
     """The same definition for a handful of sampled rows of one sequence:
     q_rows [R, D], heads [R], positions [R]. Used where the full output is
     too large for the oracle (rows are independent)."""
@@ -117,8 +153,12 @@ def attend_rows(q_rows, heads, positions, seq_ctx, k_cache, v_cache, block_table
             cache[g] = paged.gather(k_cache, v_cache, block_table, seq_ctx, g, fmt,
                                     k_scale, v_scale)
         K, V = cache[g]
-        ob, _, _, _ = _rows_attend(np.asarray(q_rows[r:r + 1], dtype=np.float64),
-                                   np.array([pos]), K, V, scale)
+        qr = np.asarray(q_rows[r:r + 1], dtype=np.float64)
+        if window is None:
+            ob, _, _, _ = _rows_attend(qr, np.array([pos]), K, V, scale)
+        else:
+            lo, hi = _row_keys(np.array([pos]), seq_ctx, window)
+            ob, _, _, _ = _rows_attend_range(qr, lo, hi, K, V, scale)
         out[r] = ob[0]
     return out
 
@@ -140,6 +180,17 @@ def verify(q, ctx_lens, k_cache, v_cache, block_tables, fmt, num_kv_heads,
     o, m, l = attend(q.reshape(B * qlen, Hq, D), [qlen] * B, ctx_lens, k_cache,
                      v_cache, block_tables, fmt, num_kv_heads, softmax_scale,
                      k_scale, v_scale)
+    return o.reshape(B, qlen, Hq, D)
+
+
+def window_attend(q, ctx_lens, k_cache, v_cache, block_tables, fmt, num_kv_heads,
+                  softmax_scale, window, k_scale=None, v_scale=None):
+    """q [B, q_len, Hq, D]: the q_len newest positions of each sequence, each
+    attending non-causally to its sliding window (the draft attention)."""
+    B, qlen, Hq, D = q.shape
+    o, m, l = attend(q.reshape(B * qlen, Hq, D), [qlen] * B, ctx_lens, k_cache, v_cache,
+                     block_tables, fmt, num_kv_heads, softmax_scale, k_scale, v_scale,
+                     window=window)
     return o.reshape(B, qlen, Hq, D)
 
 
