@@ -29,6 +29,11 @@
 // * The 4 waves' (m, l, O) are merged through LDS, and each work-group writes
 //   one partial per row; the combine kernel merges the partitions in a fixed
 //   order, so results are bitwise reproducible.
+// * The same kernels run the draft model's non-causal sliding-window attention
+//   ("1Cat-vLLM 1.5.0", "Production DFlash2 on V100"; "Flash-V100 long-context
+//   improvements": prefix tiles outside the window are skipped): rows see keys
+//   pos - W .. ctx - 1, and the partitions start at the first tile any row of
+//   the sequence can see, so the prefix before the window is never read.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -130,7 +135,13 @@ void decode_split_kernel(const DecodeArgs a) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int rows = a.q_len * G;
   const int ctx = a.context_lens[b];
-  const int tb = p * a.part_len;
+  // Rows are causal (window < 0), or see the keys pos - window .. ctx - 1 (the
+  // non-causal sliding window). With a window the partitions tile the keys
+  // from the first one any row can see, rounded down to a tile: everything
+  // before it is never loaded.
+  const bool win = a.window >= 0;
+  const int lo_seq = win ? (max(0, ctx - a.q_len - a.window) & ~63) : 0;
+  const int tb = lo_seq + p * a.part_len;
   const int te = min(tb + a.part_len, ctx);
   const int ntiles = te > tb ? (te - tb + 63) >> 6 : 0;
   const int J = ntiles > w ? (ntiles - w + 3) >> 2 : 0;  // tiles of this wave: w + 4 j
@@ -139,10 +150,13 @@ void decode_split_kernel(const DecodeArgs a) {
   const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
   const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
   const int64_t kv_heads = a.num_kv_heads;
-  const int first_masked = ctx - a.q_len + 1;  // smallest key some row cannot see
+  const int first_masked = ctx - a.q_len + 1;  // causal: smallest key some row cannot see
+  const int last_lo = ctx - 1 - a.window;      // window: largest first visible key of a row
 
   auto tile_t0 = [&](int j) { return tb + ((w + 4 * j) << 6); };
-  auto need_mask = [&](int t0) { return t0 + 64 > first_masked; };
+  auto need_mask = [&](int t0) {
+    return win ? (t0 + 64 > ctx || t0 < last_lo) : t0 + 64 > first_masked;
+  };
 
   // Page ids of tile j (loaded one tile before they are used).
   auto pages = [&](int j) {
@@ -269,12 +283,16 @@ void decode_split_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
         const int r = nb * 16 + c;
-        const int lim = min(ctx - a.q_len + r / G, ctx - 1);
+        const int pos = ctx - a.q_len + r / G;
+        const int lim_lo = win ? pos - a.window : 0;
+        const int lim_hi = win ? ctx - 1 : min(pos, ctx - 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t0 + 16 * qg + 4 * s + i > lim) sacc[nb][s][i] = kNegInf;
+          for (int i = 0; i < 4; ++i) {
+            const int key = t0 + 16 * qg + 4 * s + i;
+            if (key > lim_hi || key < lim_lo) sacc[nb][s][i] = kNegInf;
+          }
       }
     }
 #pragma unroll

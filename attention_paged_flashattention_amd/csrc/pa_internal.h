@@ -39,6 +39,7 @@ struct DecodeArgs {
   int bs_log2;
   int part_len;             // tokens per partition, a multiple of 64
   int num_parts;
+  int window;               // -1: causal rows; W >= 0: non-causal window of W keys
   float softmax_scale;
 };
 

@@ -143,6 +143,14 @@ void partition_shape(int requested, int max_ctx, int* part_len, int* parts) {
   *parts = (int)std::max<int64_t>(1, (max_ctx + len - 1) / len);
 }
 
+// Keys a sequence's partitions must cover: the whole context, or with a
+// window of W keys the W + q_len keys of the widest row set, plus one tile for
+// rounding the start down to a tile boundary.
+int key_span(int max_ctx, int q_len, int window) {
+  if (window < 0) return max_ctx;
+  return (int)std::min<int64_t>(max_ctx, (int64_t)window + q_len + kTile);
+}
+
 size_t ws_bytes(int64_t rows, int parts, int head_dim) {
   const size_t ml = (size_t)rows * parts * 2 * sizeof(float);
   const size_t ml_al = (ml + 255) / 256 * 256;
@@ -155,7 +163,8 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
                       const int32_t* context_lens, int max_context_len, int hq, int hkv,
                       int head_dim, const float* k_scale, const float* v_scale,
                       float softmax_scale, int num_partitions, void* workspace,
-                      size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream) {
+                      size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream,
+                      int window = -1) {
   if (batch < 0) return fail(PA_ERR_INVALID_ARG, "%s: batch must be >= 0", name);
   if (q_len <= 0) return fail(PA_ERR_INVALID_ARG, "%s: q_len must be positive", name);
   if (num_partitions < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_partitions must be >= 0", name);
@@ -170,9 +179,10 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
   if (num_partitions > kMaxParts)
     return fail(PA_ERR_UNSUPPORTED, "%s: at most %d partitions", name, kMaxParts);
   if (batch == 0) return ok();
-  const int req = num_partitions ? num_partitions : auto_partitions(batch, q_len, hkv, max_context_len);
+  const int span = key_span(max_context_len, q_len, window);
+  const int req = num_partitions ? num_partitions : auto_partitions(batch, q_len, hkv, span);
   int part_len = 0, parts = 0;
-  partition_shape(req, max_context_len, &part_len, &parts);
+  partition_shape(req, span, &part_len, &parts);
   const int64_t rows = (int64_t)batch * q_len * hq;
   const size_t need = ws_bytes(rows, parts, head_dim);
   if (!workspace) return fail(PA_ERR_INVALID_ARG, "%s: workspace is null", name);
@@ -202,6 +212,7 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
   a.bs_log2 = log2i(block_size);
   a.part_len = part_len;
   a.num_parts = parts;
+  a.window = window < 0 ? -1 : std::min(window, max_context_len);
   a.softmax_scale = softmax_scale;
   const int nrows = q_len * G;
   const int nqb = nrows <= 16 ? 1 : (nrows <= 32 ? 2 : 4);
@@ -366,6 +377,24 @@ PA_API pa_status attn_verify_paged(const void* q, pa_dtype q_dtype, int batch, i
                      out_dtype, stream);
 }
 
+PA_API pa_status attn_window_paged(const void* q, pa_dtype q_dtype, int batch, int q_len,
+                                   int window_left, const void* key_cache,
+                                   const void* value_cache, pa_dtype cache_dtype, int block_size,
+                                   int64_t num_blocks, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens,
+                                   int max_context_len, int num_q_heads, int num_kv_heads,
+                                   int head_dim, const float* k_scale, const float* v_scale,
+                                   float softmax_scale, int num_partitions, void* workspace,
+                                   size_t workspace_bytes, void* out, pa_dtype out_dtype,
+                                   void* stream) {
+  if (window_left < 0) return fail(PA_ERR_INVALID_ARG, "attn_window_paged: window_left must be >= 0");
+  return decode_like("attn_window_paged", q, q_dtype, batch, q_len, key_cache, value_cache,
+                     cache_dtype, block_size, num_blocks, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_q_heads, num_kv_heads, head_dim, k_scale,
+                     v_scale, softmax_scale, num_partitions, workspace, workspace_bytes, out,
+                     out_dtype, stream, window_left);
+}
+
 PA_API int pa_decode_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads,
                                 int head_dim, int max_context_len) {
   (void)num_q_heads;
@@ -392,6 +421,20 @@ PA_API size_t pa_workspace_bytes(int op, int batch, int q_len, int num_q_heads, 
   return ws_bytes((int64_t)batch * q_len * num_q_heads, parts, head_dim);
 }
 
+PA_API size_t pa_window_workspace_bytes(int batch, int q_len, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int num_partitions, int max_context_len,
+                                        int window_left) {
+  if (batch <= 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_partitions < 0 || max_context_len < 0 || window_left < 0)
+    return 0;
+  const int span = key_span(max_context_len, q_len, window_left);
+  const int req = num_partitions ? num_partitions
+                                 : auto_partitions(batch, q_len, num_kv_heads, span);
+  int part_len = 0, parts = 0;
+  partition_shape(req, span, &part_len, &parts);
+  return ws_bytes((int64_t)batch * q_len * num_q_heads, parts, head_dim);
+}
+
 PA_API int pa_supports(int op, pa_dtype q_dtype, pa_dtype cache_dtype, int head_dim,
                        int num_q_heads, int num_kv_heads, int block_size, int q_len) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
@@ -408,7 +451,7 @@ PA_API int pa_supports(int op, pa_dtype q_dtype, pa_dtype cache_dtype, int head_
   if (head_dim != 64 && head_dim != 128) return 0;
   if (op == PA_OP_PREFILL) return q_len >= 0 && G <= 32 && is_pow2(G);
   if (op == PA_OP_DECODE) return q_len == 1 && G <= kMaxRows;
-  if (op == PA_OP_VERIFY) return q_len >= 1 && (int64_t)q_len * G <= kMaxRows;
+  if (op == PA_OP_VERIFY || op == PA_OP_WINDOW) return q_len >= 1 && (int64_t)q_len * G <= kMaxRows;
   return 0;
 }
 

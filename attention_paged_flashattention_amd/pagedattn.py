@@ -19,13 +19,14 @@ PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, 1, 2, 3
 # pa_dtype
 PA_F16, PA_BF16, PA_F32, PA_FP8_E4M3, PA_FP8_E5M2 = 0, 1, 2, 3, 4
 # pa_op
-PA_OP_WRITE, PA_OP_PREFILL, PA_OP_DECODE, PA_OP_VERIFY = 0, 1, 2, 3
+PA_OP_WRITE, PA_OP_PREFILL, PA_OP_DECODE, PA_OP_VERIFY, PA_OP_WINDOW = 0, 1, 2, 3, 4
 
 CACHE_DTYPES = {"f16": PA_F16, "e4m3": PA_FP8_E4M3, "e5m2": PA_FP8_E5M2}
 TORCH_DTYPES = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float32: PA_F32}
 
 EXPORTS = ["kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
-           "attn_verify_paged", "pa_decode_partitions", "pa_workspace_bytes",
+           "attn_verify_paged", "attn_window_paged", "pa_window_workspace_bytes",
+           "pa_decode_partitions", "pa_workspace_bytes",
            "pa_supports", "pa_last_error", "pa_version", "pa_validate_tables",
            "pa_profile_next_call"]
 
@@ -54,6 +55,9 @@ _DECODE_TAIL = [_vp, _vp, _i32, _i32, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _i
                 _f32, _i32, _vp, _sz, _vp, _i32, _vp]
 _lib.attn_decode_paged.argtypes = [_vp, _i32, _i32] + _DECODE_TAIL
 _lib.attn_verify_paged.argtypes = [_vp, _i32, _i32, _i32] + _DECODE_TAIL
+_lib.attn_window_paged.argtypes = [_vp, _i32, _i32, _i32, _i32] + _DECODE_TAIL
+_lib.pa_window_workspace_bytes.argtypes = [_i32] * 8
+_lib.pa_window_workspace_bytes.restype = _sz
 _lib.pa_decode_partitions.argtypes = [_i32] * 6
 _lib.pa_decode_partitions.restype = _i32
 _lib.pa_workspace_bytes.argtypes = [_i32] * 8
@@ -66,7 +70,7 @@ _lib.pa_validate_tables.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i64, _vp]
 _lib.pa_profile_next_call.argtypes = [_vp, _vp]
 _lib.pa_profile_next_call.restype = None
 for _name in ("kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
-              "attn_verify_paged", "pa_validate_tables"):
+              "attn_verify_paged", "attn_window_paged", "pa_validate_tables"):
     getattr(_lib, _name).restype = _i32
 
 
@@ -211,6 +215,12 @@ def pa_workspace_bytes(op, batch, q_len, num_q_heads, num_kv_heads, head_dim, nu
                                        num_partitions, max_context_len))
 
 
+def pa_window_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads, head_dim, num_partitions,
+                              max_context_len, window_left):
+    return int(_lib.pa_window_workspace_bytes(batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                              num_partitions, max_context_len, window_left))
+
+
 def pa_decode_partitions(batch, q_len, num_q_heads, num_kv_heads, head_dim, max_context_len):
     return int(_lib.pa_decode_partitions(batch, q_len, num_q_heads, num_kv_heads, head_dim,
                                          max_context_len))
@@ -223,13 +233,17 @@ def pa_supports(op, q_dtype, cache_dtype, head_dim, num_q_heads, num_kv_heads, b
 
 def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_tables, context_lens,
                  max_context_len, softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
-                 out_dtype, stream, bind=False):
+                 out_dtype, stream, bind=False, window=None):
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
     batch = q.shape[0]
     hq, d = q.shape[-2], q.shape[-1]
     nb, hkv, bs, _ = key_cache.shape
-    need = pa_workspace_bytes(op, batch, q_len, hq, hkv, d, num_partitions, max_context_len)
+    if op == PA_OP_WINDOW:
+        need = pa_window_workspace_bytes(batch, q_len, hq, hkv, d, num_partitions,
+                                         max_context_len, window)
+    else:
+        need = pa_workspace_bytes(op, batch, q_len, hq, hkv, d, num_partitions, max_context_len)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     out = _out(q, out, out_dtype, tuple(q.shape))
@@ -240,6 +254,8 @@ def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_ta
             TORCH_DTYPES[out.dtype], _stream(q.device, stream)]
     if op == PA_OP_DECODE:
         args = [_ptr(q), TORCH_DTYPES[q.dtype], batch] + args
+    elif op == PA_OP_WINDOW:
+        args = [_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len, int(window)] + args
     else:
         args = [_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len] + args
     if bind:
@@ -290,6 +306,29 @@ def attn_verify_paged(q, key_cache, value_cache, cache_dtype, block_tables, cont
                         value_cache, cache_dtype, block_tables, context_lens, max_context_len,
                         softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
                         out_dtype, stream)
+
+
+def attn_window_paged(q, window_left, key_cache, value_cache, cache_dtype, block_tables,
+                      context_lens, max_context_len, softmax_scale, k_scale=None, v_scale=None,
+                      num_partitions=0, workspace=None, out=None, out_dtype=None, stream=None):
+    """q [B, q_len, Hq, D] -> out [B, q_len, Hq, D]; row i of sequence b sees
+    keys pos - window_left .. ctx_b - 1 (pos = ctx_b - q_len + i)."""
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    return _decode_like(_lib.attn_window_paged, PA_OP_WINDOW, q, q.shape[1], key_cache,
+                        value_cache, cache_dtype, block_tables, context_lens, max_context_len,
+                        softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
+                        out_dtype, stream, window=window_left)
+
+
+def bind_attn_window_paged(q, window_left, key_cache, value_cache, cache_dtype, block_tables,
+                           context_lens, max_context_len, softmax_scale, k_scale=None,
+                           v_scale=None, num_partitions=0, workspace=None, out=None,
+                           out_dtype=None, stream=None):
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    return _decode_like(_lib.attn_window_paged, PA_OP_WINDOW, q, q.shape[1], key_cache,
+                        value_cache, cache_dtype, block_tables, context_lens, max_context_len,
+                        softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
+                        out_dtype, stream, bind=True, window=window_left)
 
 
 def pa_profile_next_call(start_event, stop_event):

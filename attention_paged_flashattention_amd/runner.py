@@ -92,6 +92,16 @@ class DeviceCase:
                                     num_partitions=num_partitions, workspace=workspace, out=out,
                                     out_dtype=out_dtype, stream=stream)
 
+    def window(self, q_len, window_left, num_partitions=0, workspace=None, out=None,
+               out_dtype=None, stream=None):
+        c = self.case
+        q = self.q.view(c.batch, q_len, c.num_q_heads, c.head_dim)
+        return pa.attn_window_paged(q, window_left, self.key_cache, self.value_cache, c.cache_fmt,
+                                    self.block_tables, self.ctx_lens, self.max_ctx,
+                                    c.softmax_scale, self.k_scale, self.v_scale,
+                                    num_partitions=num_partitions, workspace=workspace, out=out,
+                                    out_dtype=out_dtype, stream=stream)
+
     def prefill(self, q_rows, cu_seqlens, max_q_len, ctx_lens, max_ctx, out=None, out_dtype=None,
                 stream=None):
         c = self.case

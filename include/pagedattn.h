@@ -91,7 +91,8 @@ typedef enum pa_op {
   PA_OP_WRITE = 0,
   PA_OP_PREFILL = 1,
   PA_OP_DECODE = 2,
-  PA_OP_VERIFY = 3
+  PA_OP_VERIFY = 3,
+  PA_OP_WINDOW = 4
 } pa_op;
 
 /*
@@ -196,6 +197,45 @@ PA_API pa_status attn_verify_paged(
     int num_partitions, void* workspace, size_t workspace_bytes,
     void* out, pa_dtype out_dtype, void* stream);
 
+/*
+ * Non-causal sliding-window attention over the paged cache: the draft model's
+ * attention of the "1Cat-vLLM 1.5.0" notes ("Production DFlash2 on V100":
+ * non-causal sliding-window draft attention; "Flash-V100 long-context
+ * improvements": prefix tiles outside the window are skipped). The pages give
+ * no formula; the reading implemented is the usual left window without a
+ * causal mask: query i of sequence b sits at pos = context_lens[b] - q_len + i
+ * and attends every key j with
+ *
+ *     pos - window_left <= j < context_lens[b]
+ *
+ * (window_left keys before its own position, itself, and every later key of
+ * its block). Pages holding only keys before the window are never read.
+ *
+ *   q            [batch][q_len][num_q_heads][head_dim]
+ *   out          [batch][q_len][num_q_heads][head_dim]
+ *   window_left  >= 0 (PA_ERR_INVALID_ARG otherwise); a window at least as
+ *                long as the context is full non-causal attention
+ *   q_len        1 <= q_len, q_len * (num_q_heads / num_kv_heads) <= 64
+ *   workspace    at least pa_window_workspace_bytes(...) bytes
+ * Other arguments as in attn_decode_paged.
+ */
+PA_API pa_status attn_window_paged(
+    const void* q, pa_dtype q_dtype, int batch, int q_len, int window_left,
+    const void* key_cache, const void* value_cache, pa_dtype cache_dtype,
+    int block_size, int64_t num_blocks,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int max_context_len,
+    int num_q_heads, int num_kv_heads, int head_dim,
+    const float* k_scale, const float* v_scale, float softmax_scale,
+    int num_partitions, void* workspace, size_t workspace_bytes,
+    void* out, pa_dtype out_dtype, void* stream);
+
+/* Bytes of workspace attn_window_paged needs for these arguments
+ * (num_partitions = 0 means automatic); 0 for invalid arguments. */
+PA_API size_t pa_window_workspace_bytes(int batch, int q_len, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int num_partitions,
+                                        int max_context_len, int window_left);
+
 /* Partition count that num_partitions = 0 selects for decode/verify (host). */
 PA_API int pa_decode_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads,
                                 int head_dim, int max_context_len);
@@ -208,7 +248,8 @@ PA_API size_t pa_workspace_bytes(int op, int batch, int q_len, int num_q_heads,
                                  int max_context_len);
 
 /* 1 if a kernel covers this combination, else 0. q_len is the per-sequence
- * query count (1 for decode, the verify width, the chunk for prefill). */
+ * query count (1 for decode, the verify or window block width, the chunk for
+ * prefill). */
 PA_API int pa_supports(int op, pa_dtype q_dtype, pa_dtype cache_dtype, int head_dim,
                        int num_q_heads, int num_kv_heads, int block_size, int q_len);
 

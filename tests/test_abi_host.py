@@ -204,3 +204,52 @@ def test_partitions_and_workspace(pa):
     assert pa.pa_workspace_bytes(pa.PA_OP_PREFILL, 1, 4096, 32, 8, 128, 0, 32768) == 0
     assert pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 16, 131072) == \
         (4 * 8 * 32 * 16 * 2 * 4 + 255) // 256 * 256 + 4 * 8 * 32 * 16 * 128 * 4
+
+
+def _call_window(pa, q_len, window, **kw):
+    a = _decode_args(**kw)
+    return pa.lib().attn_window_paged(a["q"], a["q_dtype"], a["batch"], q_len, window, a["kc"],
+                                      a["vc"], a["cache_dtype"], a["bs"], a["nb"], a["bt"],
+                                      a["maxblk"], a["ctx"], a["maxctx"], a["hq"], a["hkv"], a["d"],
+                                      a["ks"], a["vs"], a["scale"], a["parts"], a["ws"], a["wsb"],
+                                      a["out"], a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("q_len,window,kw,status", [
+    (8, -1, {}, 1),                       # negative window
+    (8, 16, dict(q=NUL), 1),
+    (0, 16, {}, 1),                       # q_len must be positive
+    (17, 16, {}, 2),                      # 17 * G(4) rows exceed one group
+    (8, 16, dict(d=96), 2),
+    (8, 16, dict(wsb=16), 1),
+    (8, 16, dict(maxctx=65), 1),
+])
+def test_window_rejects_before_launch(pa, q_len, window, kw, status):
+    assert _call_window(pa, q_len, window, **kw) == status
+    assert pa.pa_last_error() != ""
+
+
+def test_window_batch_zero_is_a_noop(pa):
+    assert _call_window(pa, 8, 16, batch=0) == 0
+
+
+def test_window_workspace_covers_only_the_window(pa):
+    """The partitions of the window call tile the W + q_len keys a sequence's
+    rows can see (plus one tile of rounding), so a short window over a long
+    context needs a short workspace; a window longer than the context needs
+    what the verify call needs."""
+    ctx = 131072
+    full = pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 0, ctx)
+    assert pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 0, ctx, 10 ** 6) == full
+    small = pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 0, ctx, 4096)
+    assert 0 < small < full
+    # explicit partitions: the same count as verify over the window's span
+    assert pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 2, ctx, 4096) == \
+        pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 2, 4096 + 8 + 64)
+    assert pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 0, ctx, -1) == 0
+
+
+def test_supports_window(pa):
+    assert pa.pa_supports(pa.PA_OP_WINDOW, 0, 4, 128, 32, 8, 2048, 8)
+    assert pa.pa_supports(pa.PA_OP_WINDOW, 0, 3, 128, 32, 8, 16, 16)
+    assert not pa.pa_supports(pa.PA_OP_WINDOW, 0, 3, 128, 32, 8, 16, 17)

@@ -285,3 +285,82 @@ def test_prefill_is_bitwise_deterministic(runner):
     b = dc.prefill(dc.q, cu, 1500, dc.ctx_lens, 1500, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# non-causal sliding window (the draft attention): rows see pos - W .. ctx - 1
+# ---------------------------------------------------------------------------
+
+WINDOW_CASES = [
+    # fmt, B, ctx, q_len, W, Hq, Hkv, D, bs, q_dtype, partitions
+    ("e5m2", 2, (300, 5000), 8, 1000, 32, 8, 128, 2048, "f16", 0),
+    ("e4m3", 3, (50, 700, 1500), 4, 63, 32, 8, 128, 16, "f16", 0),
+    ("f16", 2, (65, 300), 1, 0, 4, 1, 64, 16, "f16", 0),
+    ("e4m3", 1, (4097,), 16, 200, 32, 8, 128, 64, "f16", 3),
+    ("e4m3", 2, (100, 900), 8, 5000, 32, 8, 128, 16, "bf16", 0),
+    ("e5m2", 2, (129, 2100), 8, 7, 16, 4, 64, 32, "f16", 2),
+]
+
+
+def _oracle_window(case, W):
+    from oracle import attention
+    from tests.oracle_helpers import q_f32
+    kc, vc = oracle_cache(case)
+    o, _, _ = attention.attend(q_f32(case), case.q_lens, case.ctx_lens, kc, vc,
+                               case.block_tables, case.cache_fmt, case.num_kv_heads,
+                               case.softmax_scale, case.k_scale, case.v_scale, window=W)
+    return o
+
+
+@pytest.mark.parametrize("fmt,B,ctx,q_len,W,Hq,Hkv,D,bs,q_dtype,parts", WINDOW_CASES)
+def test_window_parity(runner, fmt, B, ctx, q_len, W, Hq, Hkv, D, bs, q_dtype, parts):
+    log(f"window {fmt} B={B} ctx={ctx} q_len={q_len} W={W} Hq={Hq} Hkv={Hkv} D={D} bs={bs} "
+        f"q={q_dtype} P={parts}")
+    case = _mk(fmt, B, ctx, q_len, Hq, Hkv, D, bs, q_dtype, sigma_kv=0.5)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.window(q_len, W, num_partitions=parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = _oracle_window(case, W).reshape(B, q_len, Hq, D)
+    check_close(out, ref, fmt, "window f32")
+    qt = torch.float16 if q_dtype == "f16" else torch.bfloat16
+    out16 = dc.window(q_len, W, num_partitions=parts)
+    check_close(out16, ref, fmt, "window q-dtype", out_dtype=qt)
+
+
+def test_window_never_reads_the_prefix(runner):
+    """Pages that hold only keys older than every row's window are poisoned
+    with NaN codes after the writes; a read of any of them would turn the
+    output into NaN (masked keys still multiply their values by zero)."""
+    W, q_len = 300, 8
+    case = _mk("e4m3", 2, (6000, 9000), q_len, bs=64)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    clean = dc.window(q_len, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    bs = case.block_size
+    for b in range(2):
+        ctx = int(case.ctx_lens[b])
+        first_seen = ctx - q_len - W
+        for blk in range(first_seen // bs - 1):   # pages wholly before the window's first tile
+            page = int(case.block_tables[b][blk])
+            dc.key_cache[page].fill_(synth.POISON["e4m3"])
+            dc.value_cache[page].fill_(synth.POISON["e4m3"])
+    out = dc.window(q_len, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    assert torch.equal(out, clean)
+
+
+def test_window_covering_the_context_equals_last_position_decode(runner):
+    """A window longer than the context makes every row of the block see all
+    ctx keys: each row equals a decode of the same query at the last position
+    (same kernels; compared within the fp16 rounding of P)."""
+    case = _mk("e5m2", 2, (300, 2100), 8, 32, 8, 128, 64, "f16", sigma_kv=0.5)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.window(8, 10 ** 6, out_dtype=torch.float32)
+    qv = dc.q.view(2, 8, 32, 128)
+    for i in range(8):
+        od = dc.decode(q=qv[:, i].contiguous(), out_dtype=torch.float32)
+        assert torch.max(torch.abs(od - out[:, i])).item() < 1e-4
