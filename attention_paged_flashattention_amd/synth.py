@@ -276,6 +276,17 @@ def chunked_prefill_64k(seed=1009, total=65536, chunk=4096):
                      32, 8, 128, 2048, "bf16", "bf16", "e4m3", meta=dict(chunk=chunk))
 
 
+def window_draft_q8(seed=1010, ctx=131072, window=4096, batch=4):
+    """Draft attention: 4 sequences, blocks of 8 new queries each attending
+    non-causally to a 4096-key sliding window (plus the later keys of their
+    block) at the given context, E5M2 KV (no scales), fp16 Q ~ N(0,1), K/V ~
+    N(0, 0.5), 2048-token pages. The window length and the block width are
+    readings (the pages give neither); the block is the verifier's q8."""
+    return make_case(f"window{window // 1024}k_q8_b{batch}_{ctx // 1024}k_e5m2_bs2048", seed,
+                     [ctx] * batch, 8, 32, 8, 128, 2048, "f16", "f16", "e5m2", sigma_kv=0.5,
+                     meta=dict(window=window))
+
+
 WORKLOADS = {
     1: prefill_decode_small,
     2: batched_decode_e4m3,
@@ -286,4 +297,5 @@ WORKLOADS = {
     "b16": batched_decode_e5m2_16k,
     "q16": verify_q16_128k,
     "64k": chunked_prefill_64k,
+    "win": window_draft_q8,
 }

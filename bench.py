@@ -12,8 +12,8 @@ cache are used in rotation so that no step finds its cache in the 256 MB
 last-level cache. The same line carries the 32K chunked-prefill throughput
 (useful causal TFLOP/s; one step = 8 chunks of 4096 tokens, each a write then a
 prefill), the q8 and q16 verify at 128K, the 256K decode, the batched decodes
-(8 x 1K-4K E4M3, 16 x 16K E5M2), the 64K prefill in 4096- and 8192-token
-chunks, the write kernel's rate, the small prefill+decode workload's latency,
+(8 x 1K-4K E4M3, 16 x 16K E5M2), the draft's sliding-window attention at 32K
+and 128K, the 64K prefill in 4096- and 8192-token chunks, the write kernel's rate, the small prefill+decode workload's latency,
 the cost of a decode call with nothing to read, the roofline of the dominant
 kernels, and the CPU oracle timed on a bounded sample of the headline
 workload.
@@ -42,7 +42,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS_16 = 2500.0    # MI355X dense fp16 / bf16 MFMA
 METRIC = "paged-attn decode GB/s (%HBM peak) @128K FP8 KV; prefill TFLOP/s @32K"
 SECTIONS = ["decode128k", "prefill32k", "verify128k", "verify_q16", "decode256k", "decode_b8",
-            "decode_b16", "prefill64k", "small", "empty", "copy"]
+            "decode_b16", "window", "prefill64k", "small", "empty", "copy"]
 
 
 def log(msg):
@@ -132,9 +132,10 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
 
 
-def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
-    """Write the newest q_len tokens of every sequence, then decode/verify.
-    Returns a result dict with the step time and the split kernel's times."""
+def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=None):
+    """Write the newest q_len tokens of every sequence, then decode/verify
+    (or the sliding-window attention when ``window`` is set). Returns a result
+    dict with the step time and the split kernel's times."""
     import torch
     from attention_paged_flashattention_amd import pagedattn as pa
     from attention_paged_flashattention_amd import runner
@@ -147,15 +148,24 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
     k_new, v_new, s_new = dc.k[newest].contiguous(), dc.v[newest].contiguous(), dc.slots[newest].contiguous()
     c = case
     parts = c.meta.get("partitions", 0)
-    op = pa.PA_OP_DECODE if q_len == 1 else pa.PA_OP_VERIFY
-    wsb = pa.pa_workspace_bytes(op, c.batch, q_len, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                parts, dc.max_ctx)
+    if window is not None:
+        wsb = pa.pa_window_workspace_bytes(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
+                                           c.head_dim, parts, dc.max_ctx, window)
+    else:
+        op = pa.PA_OP_DECODE if q_len == 1 else pa.PA_OP_VERIFY
+        wsb = pa.pa_workspace_bytes(op, c.batch, q_len, c.num_q_heads, c.num_kv_heads,
+                                    c.head_dim, parts, dc.max_ctx)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dc.device)
-    qv = dc.q if q_len == 1 else dc.q.view(c.batch, q_len, c.num_q_heads, c.head_dim)
+    qv = dc.q if (q_len == 1 and window is None) else dc.q.view(c.batch, q_len, c.num_q_heads,
+                                                                 c.head_dim)
     out = torch.empty_like(qv)
     starts = [ev.create() for _ in range(steps)]
     stops = [ev.create() for _ in range(steps)]
-    bind_attn = pa.bind_attn_decode_paged if q_len == 1 else pa.bind_attn_verify_paged
+    if window is not None:
+        def bind_attn(*args, **kw):
+            return pa.bind_attn_window_paged(args[0], window, *args[1:], **kw)
+    else:
+        bind_attn = pa.bind_attn_decode_paged if q_len == 1 else pa.bind_attn_verify_paged
     # arguments marshalled once per cache copy: the timed loop only issues calls
     writes = [pa.bind_kv_cache_write_fp8(k_new, v_new, s_new, kcs[i], vcs[i], c.cache_fmt,
                                          dc.k_scale, dc.v_scale) for i in range(copies)]
@@ -177,11 +187,12 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
     ms = timed(lambda i, rec: step(i, False), steps, warmup)
     ms_ev = timed(step, steps, 0)
     kern = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
-    kv_bytes = int(sum(int(x) for x in c.ctx_lens)) * c.num_kv_heads * c.head_dim * 2 * \
-        (1 if c.cache_fmt != "f16" else 2)
+    # keys the rows can see: the whole context, or the window plus the block
+    seen = [int(x) if window is None else min(int(x), window + q_len) for x in c.ctx_lens]
+    kv_bytes = sum(seen) * c.num_kv_heads * c.head_dim * 2 * (1 if c.cache_fmt != "f16" else 2)
     rows = c.batch * q_len * c.num_q_heads
     qo = rows * c.head_dim * 2
-    meta = sum(-(-int(x) // c.block_size) for x in c.ctx_lens) * 4 + \
+    meta = sum(-(-int(x) // c.block_size) for x in seen) * 4 + \
         (0 if c.k_scale is None else 2 * c.num_kv_heads * 4)
     newest_n = len(newest)
     write_bytes = newest_n * c.num_kv_heads * c.head_dim * (2 * 2 + 2) + newest_n * 8
@@ -196,8 +207,9 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name):
                 split_us_p90=pct(kern, 90) * 1e3,
                 split_ms=kern_ms, split_bytes=split_bytes,
                 split_GBps=split_bytes / kern_ms / 1e6,
-                partitions=pa.pa_decode_partitions(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
-                                                   c.head_dim, dc_max(c)) if parts == 0 else parts)
+                partitions=(pa.pa_decode_partitions(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
+                                                    c.head_dim, dc_max(c)) if window is None else
+                            None) if parts == 0 else parts)
 
 
 def dc_max(c):
@@ -496,6 +508,12 @@ def main():
         log("section decode_b16")
         res["decode_b16"] = decode_like_section(ev, synth.batched_decode_e5m2_16k(), K, W, 2, 1,
                                                 "decode_b16_16k_e5m2_bs16")
+    if "window" in sections:
+        for ctx in (32768, 131072):
+            log(f"section window ctx {ctx}")
+            wc = synth.window_draft_q8(ctx=ctx)
+            res[f"window_{ctx}"] = decode_like_section(ev, wc, K, W, 1, 8, wc.name,
+                                                       window=wc.meta["window"])
     if "prefill64k" in sections:
         for chunk in (4096, 8192):
             log(f"section prefill64k chunk {chunk}")
@@ -575,6 +593,15 @@ def main():
                                                       round(r["split_us_p50"], 2),
                                                       round(r["split_us_p90"], 2)],
                              "partitions": r["partitions"]}
+    for ctx in (32768, 131072):
+        r = res.get(f"window_{ctx}")
+        if r:
+            line[f"window_draft_q8_{ctx // 1024}k"] = {
+                "workload": r["name"], "window": 4096, "GBps": round(r["GBps"], 1),
+                "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                "split_kernel_us": round(r["split_ms"] * 1e3, 2),
+                "split_kernel_GBps": round(r["split_GBps"], 1),
+                "bytes_in_window_per_step": r["step_bytes"]}
     for chunk in (4096, 8192):
         r = res.get(f"prefill64k_{chunk}")
         if r:

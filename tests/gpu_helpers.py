@@ -79,7 +79,8 @@ def oracle_cache_heads(case, seqs_heads):
     return kc, vc
 
 
-def oracle_rows(case, kc, vc, b, q_rows_f32, heads, positions):
+def oracle_rows(case, kc, vc, b, q_rows_f32, heads, positions, window=None):
     return attention.attend_rows(q_rows_f32, heads, positions, int(case.ctx_lens[b]), kc, vc,
                                  case.block_tables[b], case.cache_fmt, case.num_q_heads,
-                                 case.num_kv_heads, case.softmax_scale, case.k_scale, case.v_scale)
+                                 case.num_kv_heads, case.softmax_scale, case.k_scale, case.v_scale,
+                                 window=window)

@@ -1,5 +1,6 @@
-"""The five workloads and the 128K decode headline at full size, in the launch
-configuration bench.py times (automatic partitions). Rows the oracle can afford
+"""The five workloads, the 128K decode headline and the second workloads
+(batched E5M2 decode, q16 verify, 64K prefill, the draft's sliding window) at
+full size, in the launch configuration bench.py times (automatic partitions). Rows the oracle can afford
 are compared element by element (whole heads of sampled sequences); every row
 is checked for properties that hold at any size: finite, and inside the convex
 hull bound |o| <= max |V| of its KV head."""
@@ -105,7 +106,7 @@ def test_workload3_chunked_prefill_32k(runner):
         check_close(got, ref, "e4m3", f"chunk {c} sampled rows")
 
 
-def _sampled_decode_check(case, dc, out, pairs):
+def _sampled_decode_check(case, dc, out, pairs, window=None):
     """Compare every row of the sampled (sequence, KV head) pairs."""
     kc, vc = oracle_cache_heads(case, pairs)
     q32 = synth.to_f32(case.q, case.q_dtype)
@@ -119,7 +120,7 @@ def _sampled_decode_check(case, dc, out, pairs):
                 heads.append(h)
                 positions.append(int(case.ctx_lens[b]) - qlen + i)
                 rows.append(q32[b * qlen + i, h])
-        ref = oracle_rows(case, kc, vc, b, np.array(rows), heads, positions)
+        ref = oracle_rows(case, kc, vc, b, np.array(rows), heads, positions, window=window)
         got = out.reshape(-1, case.num_q_heads, case.head_dim)[b * qlen:(b + 1) * qlen][:, g * G:(g + 1) * G]
         check_close(got.reshape(-1, case.head_dim), ref, case.cache_fmt, f"seq {b} kv head {g}")
 
@@ -220,3 +221,16 @@ def test_chunked_prefill_64k(runner, chunk):
         ref = oracle_rows(case, kc, vc, 0, np.array(rows_q), rows_h, rows_p)
         got = out.cpu()[torch.tensor(np.array(rows_p) - s), torch.tensor(rows_h)]
         check_close(got, ref, "e4m3", f"chunk {c} sampled rows")
+
+
+@pytest.mark.parametrize("ctx", [32768, 131072])
+def test_window_draft_q8(runner, ctx):
+    case = synth.window_draft_q8(ctx=ctx)
+    W = case.meta["window"]
+    log(f"{case.name} window {W}")
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.window(8, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _hull_check(out, dc)
+    _sampled_decode_check(case, dc, out, [(0, 1), (3, 6)], window=W)
