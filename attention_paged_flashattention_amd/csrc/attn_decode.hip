@@ -414,11 +414,11 @@ void decode_split_kernel(const DecodeArgs a) {
 //   out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
 // over the partitions in index order; empty partitions (m_p = -inf) weigh 0.
 // Times the per-head value scale. A row with no visible key is written as zeros.
-// The partition weights go to LDS first (one load per partition, spread over
-// the threads). Thread (slice sl, dimension group dg) then adds the weighted
-// partials of partitions sl, sl + SL, ... for dimensions 4dg..4dg+3, issuing
-// kCombineBatch 16-byte loads before the first add; slices are summed in a
-// fixed order, so the result does not depend on timing.
+// The partition weights go to LDS (one load per partition, spread over the
+// threads). Thread (slice sl, dimension group dg) adds the weighted partials of
+// partitions sl, sl + SL, ... for dimensions 4dg..4dg+3, kCombineBatch 16-byte
+// loads at a time; slices are summed in a fixed order, so the result does not
+// depend on timing.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineBatch = 8;
 constexpr int kMaxCombineParts = 4096;
@@ -454,6 +454,22 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   const float* ml = a.ws_ml + row * P * 2;
   const float* po = a.ws_o + row * P * D;
 
+  // The first batch of partials does not depend on the weights: its loads
+  // are issued before the max and the weights are worked out, so at the usual
+  // partition counts (P <= SL * kCombineBatch) the merge costs one round trip.
+  const int dg = t % DG, sl = t / DG;
+  f32x4 ov[kCombineBatch];
+  auto load_batch = [&](int pb) {
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int p = pb + k * SL;
+      ov[k] = p < P ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * D + 4 * dg)
+                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  load_batch(sl);
+  const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
+
   float mloc = kNegInf;
   for (int p = t; p < P; p += kCombineThreads) mloc = fmaxf(mloc, ml[2 * p]);
   const float M = block_reduce_256(mloc, red, true);
@@ -466,16 +482,9 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   }
   const float L = block_reduce_256(lloc, red, false);   // its barriers also publish sw
 
-  const int dg = t % DG, sl = t / DG;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int pb = sl; pb < P; pb += SL * kCombineBatch) {
-    f32x4 ov[kCombineBatch];
-#pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) {
-      const int p = pb + k * SL;
-      ov[k] = p < P ? *reinterpret_cast<const f32x4*>(po + (int64_t)p * D + 4 * dg)
-                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    if (pb != sl) load_batch(pb);
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) {
       const int p = pb + k * SL;
@@ -489,7 +498,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
     f32x4 o = sacc[0][dg];
 #pragma unroll
     for (int k = 1; k < SL; ++k) o += sacc[k][dg];
-    const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
     const float f = L > 0.0f ? vscale / L : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_out<OT>(a.out, row * D + 4 * dg + i, o[i] * f);

@@ -21,14 +21,20 @@ namespace pa {
 template <int ST, int FMT>
 __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h, int c) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  const int D = a.head_dim;
+  const uint16_t* ksrc = a.key + (t * a.num_kv_heads + h) * D + c * 16;
+  const uint16_t* vsrc = a.value + (t * a.num_kv_heads + h) * D + c * 16;
+  // source and scale loads first: they do not depend on the slot
+  u32x4 kr0 = ld16(ksrc), kr1 = ld16(ksrc + 8);
+  u32x4 vr0 = ld16(vsrc), vr1 = ld16(vsrc + 8);
+  const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
+  const float kdiv = ksc ? a.k_scale[h] : 1.0f;
+  const float vdiv = vsc ? a.v_scale[h] : 1.0f;
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
   const int64_t off = slot & ((1 << a.bs_log2) - 1);
-  const int D = a.head_dim;
   const int64_t bs = (int64_t)1 << a.bs_log2;
-  const uint16_t* ksrc = a.key + (t * a.num_kv_heads + h) * D + c * 16;
-  const uint16_t* vsrc = a.value + (t * a.num_kv_heads + h) * D + c * 16;
   const int64_t ph = page * a.num_kv_heads + h;
   uint8_t* kdst = a.key_cache + ((ph * bs + off) * D + c * 16) * ES;   // token row, contiguous
   // values: dimension-major inside groups of T = min(bs, 64) tokens
@@ -37,8 +43,6 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h
   uint8_t* vdst = a.value_cache +
       ((((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D + c * 16) * T + (off & (T - 1))) * ES;
 
-  u32x4 kr0 = ld16(ksrc), kr1 = ld16(ksrc + 8);
-  u32x4 vr0 = ld16(vsrc), vr1 = ld16(vsrc + 8);
   if constexpr (FMT == KV_F16) {
     // plain copy of fp16 sources
     *reinterpret_cast<u32x4*>(kdst) = kr0;
@@ -48,9 +52,6 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h
     for (int i = 0; i < 16; ++i)
       reinterpret_cast<uint16_t*>(vdst)[(int64_t)i * T] = (uint16_t)(vw[i >> 1] >> ((i & 1) * 16));
   } else {
-    const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
-    const float kdiv = ksc ? a.k_scale[h] : 1.0f;
-    const float vdiv = vsc ? a.v_scale[h] : 1.0f;
     const uint32_t kw[8] = {kr0.x, kr0.y, kr0.z, kr0.w, kr1.x, kr1.y, kr1.z, kr1.w};
     const uint32_t vw[8] = {vr0.x, vr0.y, vr0.z, vr0.w, vr1.x, vr1.y, vr1.z, vr1.w};
     uint32_t kout[4] = {0, 0, 0, 0};
@@ -86,20 +87,25 @@ __global__ __launch_bounds__(256) void kv_write_tokens_kernel(const WriteArgs a)
 template <int ST, int FMT>
 __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int q) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  // The source values and the scale do not depend on the slot: their loads
+  // are issued together with the slot's, so the write costs one round trip.
+  const int D = a.head_dim;
+  const int64_t src = ((int64_t)t * a.num_kv_heads + h) * D + 4 * q;
+  const u32x2 kr = *reinterpret_cast<const u32x2*>(a.key + src);
+  const u32x2 vr = *reinterpret_cast<const u32x2*>(a.value + src);
+  const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
+  const float kdiv = ksc ? a.k_scale[h] : 1.0f;
+  const float vdiv = vsc ? a.v_scale[h] : 1.0f;
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
   const int off = (int)(slot & ((1 << a.bs_log2) - 1));
-  const int D = a.head_dim;
-  const int64_t src = ((int64_t)t * a.num_kv_heads + h) * D + 4 * q;
   const int64_t ph = page * a.num_kv_heads + h;
   uint8_t* kdst = a.key_cache + ((ph << a.bs_log2) + off) * D * ES + 4 * q * ES;
   const int vg_log2 = a.bs_log2 < 6 ? a.bs_log2 : 6;
   const int T = 1 << vg_log2;
   uint8_t* vdst = a.value_cache +
       ((((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D + 4 * q) * T + (off & (T - 1))) * ES;
-  const u32x2 kr = *reinterpret_cast<const u32x2*>(a.key + src);
-  const u32x2 vr = *reinterpret_cast<const u32x2*>(a.value + src);
   if constexpr (FMT == KV_F16) {
     *reinterpret_cast<u32x2*>(kdst) = kr;
     uint16_t* vd = reinterpret_cast<uint16_t*>(vdst);
@@ -108,9 +114,6 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int
     vd[2 * T] = (uint16_t)vr.y;
     vd[3 * T] = (uint16_t)(vr.y >> 16);
   } else {
-    const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
-    const float kdiv = ksc ? a.k_scale[h] : 1.0f;
-    const float vdiv = vsc ? a.v_scale[h] : 1.0f;
     const uint32_t kw[2] = {kr.x, kr.y}, vw[2] = {vr.x, vr.y};
     uint32_t kout = 0;
 #pragma unroll
