@@ -8,13 +8,51 @@
 // overwritten in full, and the attention kernels never read a slot past the
 // context.
 //
-// Large writes (prefill chunks): each thread quantizes 16 consecutive head
-// dimensions of one token's K and V, consecutive tokens on consecutive lanes.
-// Small writes (a decode or verify step): each thread quantizes 4 dimensions.
+// Quantization: x / scale as the correctly rounded fp32 quotient (from the
+// correctly rounded reciprocal and one fma correction), then the fp32 value to
+// FP8 by gfx950's packed conversion after a clamp to the largest finite value
+// (round to nearest even, saturating, sign kept).
+//
+// Large writes (prefill chunks) with head_dim 64 or 128: a work-group per 64
+// tokens of one head, reading whole source rows and transposing the value
+// codes through LDS (the row kernel). Other head sizes: each thread quantizes
+// 16 consecutive dimensions of one token. Small writes (a decode or verify
+// step): each thread quantizes 4 dimensions.
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
+
+// 8 source elements (one 16-byte chunk) -> 8 cache codes: FP8 in the low 8
+// bytes, or the fp16 elements unchanged.
+template <int ST, int FMT>
+__device__ __forceinline__ u32x4 encode8(u32x4 w, bool scaled, float div, float rdiv) {
+  if constexpr (FMT == KV_F16) {
+    return w;
+  } else {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = src_to_f32<ST>((uint16_t)(ww[i >> 1] >> ((i & 1) * 16)));
+      y[i] = scaled ? div_rn(x, div, rdiv) : x;   // x / div, correctly rounded
+    }
+    return u32x4{fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]),
+                 fp8x4_from_f32<FMT>(y[4], y[5], y[6], y[7]), 0u, 0u};
+  }
+}
+
+// 4 source elements (8 bytes) -> 4 FP8 codes.
+template <int ST, int FMT>
+__device__ __forceinline__ uint32_t encode4(u32x2 w, bool scaled, float div, float rdiv) {
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = src_to_f32<ST>((uint16_t)((i < 2 ? w.x : w.y) >> ((i & 1) * 16)));
+    y[i] = scaled ? div_rn(x, div, rdiv) : x;   // x / div, correctly rounded
+  }
+  return fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]);
+}
 
 // One 16-element chunk c of token t, head h: K row (16 contiguous codes) and
 // 16 value codes (one per dimension row of the page).
@@ -30,6 +68,7 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
   const float kdiv = ksc ? a.k_scale[h] : 1.0f;
   const float vdiv = vsc ? a.v_scale[h] : 1.0f;
+  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
@@ -52,24 +91,12 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h
     for (int i = 0; i < 16; ++i)
       reinterpret_cast<uint16_t*>(vdst)[(int64_t)i * T] = (uint16_t)(vw[i >> 1] >> ((i & 1) * 16));
   } else {
-    const uint32_t kw[8] = {kr0.x, kr0.y, kr0.z, kr0.w, kr1.x, kr1.y, kr1.z, kr1.w};
-    const uint32_t vw[8] = {vr0.x, vr0.y, vr0.z, vr0.w, vr1.x, vr1.y, vr1.z, vr1.w};
-    uint32_t kout[4] = {0, 0, 0, 0};
+    const u32x4 k0 = encode8<ST, FMT>(kr0, ksc, kdiv, krcp), k1 = encode8<ST, FMT>(kr1, ksc, kdiv, krcp);
+    *reinterpret_cast<u32x4*>(kdst) = u32x4{k0.x, k0.y, k1.x, k1.y};
+    const u32x4 v0 = encode8<ST, FMT>(vr0, vsc, vdiv, vrcp), v1 = encode8<ST, FMT>(vr1, vsc, vdiv, vrcp);
+    const uint32_t vw[4] = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float x = src_to_f32<ST>((uint16_t)(kw[i >> 1] >> ((i & 1) * 16)));
-      const float y = ksc ? x / kdiv : x;   // IEEE fp32 division (correctly rounded)
-      const uint32_t code = FMT == KV_E4M3 ? f32_to_e4m3(y) : f32_to_e5m2(y);
-      kout[i >> 2] |= code << ((i & 3) * 8);
-    }
-    *reinterpret_cast<u32x4*>(kdst) = u32x4{kout[0], kout[1], kout[2], kout[3]};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float x = src_to_f32<ST>((uint16_t)(vw[i >> 1] >> ((i & 1) * 16)));
-      const float y = vsc ? x / vdiv : x;
-      const uint32_t code = FMT == KV_E4M3 ? f32_to_e4m3(y) : f32_to_e5m2(y);
-      vdst[(int64_t)i * T] = (uint8_t)code;
-    }
+    for (int i = 0; i < 16; ++i) vdst[(int64_t)i * T] = (uint8_t)(vw[i >> 2] >> ((i & 3) * 8));
   }
 }
 
@@ -80,6 +107,102 @@ __global__ __launch_bounds__(256) void kv_write_tokens_kernel(const WriteArgs a)
   const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
   if (t >= a.num_tokens) return;
   for (int c = threadIdx.x >> 6; c < a.head_dim / 16; c += 4) write_chunk<ST, FMT>(a, t, blockIdx.y, c);
+}
+
+// Many tokens, the row form: work-group = 64 consecutive tokens of one KV
+// head. Source rows are read whole (16 bytes per thread, consecutive threads
+// on consecutive bytes) and key codes go straight to their rows. Value codes
+// are transposed through LDS: when the 64 slots are consecutive and start a
+// 64-token value group (a prefill chunk's usual case) the group's D x 64 codes
+// are one contiguous block and leave with 16-byte stores; otherwise each code
+// goes to its own slot.
+constexpr int kRowTokens = 64;
+
+template <int ST, int FMT, int D>
+__global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
+  constexpr int cpt = D / 8;                        // 16-byte source chunks per token
+  constexpr int kRowIters = kRowTokens * cpt / 256;  // chunks per thread
+  constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  extern __shared__ __attribute__((aligned(16))) uint8_t vt[];   // [D][64] value codes
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kRowTokens;
+  const int ntok = (int)min<int64_t>(kRowTokens, a.num_tokens - t0);
+  const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
+  const float kdiv = ksc ? a.k_scale[h] : 1.0f;
+  const float vdiv = vsc ? a.v_scale[h] : 1.0f;
+  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
+  const int bs_mask = (1 << a.bs_log2) - 1;
+
+  // every load of the work-group first (the stores below could alias the
+  // sources as far as the compiler knows, so loads interleaved with stores
+  // would each wait for a round trip)
+  constexpr int nf = kRowTokens * cpt;
+  u32x4 kr[kRowIters], vr[kRowIters];
+  int64_t sl[kRowIters];
+#pragma unroll
+  for (int it = 0; it < kRowIters; ++it) {
+    const int f = threadIdx.x + 256 * it;
+    const int tok = f / cpt, ch = f - tok * cpt;
+    if (f < nf && tok < ntok) {
+      const int64_t t = t0 + tok;
+      const int64_t src = (t * a.num_kv_heads + h) * D + ch * 8;
+      kr[it] = ld16(a.key + src);
+      vr[it] = ld16(a.value + src);
+      sl[it] = a.slots[t];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kRowIters; ++it) {
+    const int f = threadIdx.x + 256 * it;
+    const int tok = f / cpt, ch = f - tok * cpt;
+    if (f >= nf || tok >= ntok) continue;
+    const int64_t slot = sl[it];
+    const u32x4 kc = encode8<ST, FMT>(kr[it], ksc, kdiv, krcp);
+    const u32x4 vc = encode8<ST, FMT>(vr[it], vsc, vdiv, vrcp);
+    if (slot >= 0) {
+      const int64_t ph = (slot >> a.bs_log2) * a.num_kv_heads + h;
+      uint8_t* kdst = a.key_cache + (((ph << a.bs_log2) + (slot & bs_mask)) * D + ch * 8) * ES;
+      if constexpr (ES == 2) *reinterpret_cast<u32x4*>(kdst) = kc;
+      else *reinterpret_cast<u32x2*>(kdst) = u32x2{kc.x, kc.y};
+    }
+    const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint8_t* cell = vt + ((ch * 8 + e) * kRowTokens + tok) * ES;
+      if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(cell) = (uint16_t)(vw[e >> 1] >> ((e & 1) * 16));
+      else *cell = (uint8_t)(vw[e >> 2] >> ((e & 3) * 8));
+    }
+  }
+  // one contiguous value block when the 64 slots are consecutive from the
+  // start of a value group
+  const int64_t s0 = a.slots[t0];
+  const int i = threadIdx.x;
+  const bool mine = i >= kRowTokens || (i < ntok && a.slots[t0 + i] == s0 + i);
+  const bool block = __syncthreads_and(mine) && ntok == kRowTokens && a.bs_log2 >= 6 &&
+                     s0 >= 0 && (s0 & (kRowTokens - 1)) == 0;
+  if (block) {
+    const int64_t ph = (s0 >> a.bs_log2) * a.num_kv_heads + h;
+    uint8_t* vdst = a.value_cache +
+        (((ph << (a.bs_log2 - 6)) + ((s0 & bs_mask) >> 6)) * D) * kRowTokens * ES;
+    const int n16 = D * kRowTokens * ES / 16;
+    for (int f = threadIdx.x; f < n16; f += 256)
+      reinterpret_cast<u32x4*>(vdst)[f] = reinterpret_cast<const u32x4*>(vt)[f];
+  } else {
+    const int vg_log2 = a.bs_log2 < 6 ? a.bs_log2 : 6;
+    const int T = 1 << vg_log2;
+    for (int f = threadIdx.x; f < D * kRowTokens; f += 256) {
+      const int d = f / kRowTokens, tok = f - d * kRowTokens;
+      if (tok >= ntok) continue;
+      const int64_t slot = a.slots[t0 + tok];
+      if (slot < 0) continue;
+      const int64_t ph = (slot >> a.bs_log2) * a.num_kv_heads + h;
+      const int off = (int)(slot & bs_mask);
+      uint8_t* vdst = a.value_cache +
+          ((((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D + d) * T + (off & (T - 1))) * ES;
+      if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(vdst) = *reinterpret_cast<const uint16_t*>(vt + f * 2);
+      else *vdst = vt[f];
+    }
+  }
 }
 
 // Four dimensions [4q, 4q + 4) of token t, head h: 4 key codes (one store)
@@ -96,6 +219,7 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
   const float kdiv = ksc ? a.k_scale[h] : 1.0f;
   const float vdiv = vsc ? a.v_scale[h] : 1.0f;
+  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
@@ -114,21 +238,10 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int
     vd[2 * T] = (uint16_t)vr.y;
     vd[3 * T] = (uint16_t)(vr.y >> 16);
   } else {
-    const uint32_t kw[2] = {kr.x, kr.y}, vw[2] = {vr.x, vr.y};
-    uint32_t kout = 0;
+    *reinterpret_cast<uint32_t*>(kdst) = encode4<ST, FMT>(kr, ksc, kdiv, krcp);
+    const uint32_t vcode = encode4<ST, FMT>(vr, vsc, vdiv, vrcp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = src_to_f32<ST>((uint16_t)(kw[i >> 1] >> ((i & 1) * 16)));
-      const float y = ksc ? x / kdiv : x;   // IEEE fp32 division (correctly rounded)
-      kout |= (FMT == KV_E4M3 ? f32_to_e4m3(y) : f32_to_e5m2(y)) << (i * 8);
-    }
-    *reinterpret_cast<uint32_t*>(kdst) = kout;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = src_to_f32<ST>((uint16_t)(vw[i >> 1] >> ((i & 1) * 16)));
-      const float y = vsc ? x / vdiv : x;
-      vdst[i * T] = (uint8_t)(FMT == KV_E4M3 ? f32_to_e4m3(y) : f32_to_e5m2(y));
-    }
+    for (int i = 0; i < 4; ++i) vdst[i * T] = (uint8_t)(vcode >> (i * 8));
   }
 }
 
@@ -149,10 +262,18 @@ constexpr int64_t kFewTokens = 64;
 
 template <int ST, int FMT>
 static void launch_write(const WriteArgs& a, hipStream_t s) {
+  constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  const size_t rows_lds = (size_t)a.head_dim * kRowTokens * ES;
   if (a.num_tokens < kFewTokens) {
     const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
     hipLaunchKernelGGL((kv_write_chunks_kernel<ST, FMT>), dim3((unsigned)((total + 255) / 256)),
                        dim3(256), 0, s, a);
+  } else if (a.head_dim == 64 || a.head_dim == 128) {
+    dim3 grid((unsigned)((a.num_tokens + kRowTokens - 1) / kRowTokens), (unsigned)a.num_kv_heads);
+    if (a.head_dim == 64)
+      hipLaunchKernelGGL((kv_write_rows_kernel<ST, FMT, 64>), grid, dim3(256), rows_lds, s, a);
+    else
+      hipLaunchKernelGGL((kv_write_rows_kernel<ST, FMT, 128>), grid, dim3(256), rows_lds, s, a);
   } else {
     dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads);
     hipLaunchKernelGGL((kv_write_tokens_kernel<ST, FMT>), grid, dim3(256), 0, s, a);

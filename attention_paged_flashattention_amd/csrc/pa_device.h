@@ -104,40 +104,36 @@ __device__ __forceinline__ constexpr float kv_fold() {
   return 1.0f;
 }
 
-// ---------------------------------------------------------------------------
-// fp32 -> FP8, saturating, round to nearest even. Integer rounding of the
-// fp32 bit pattern for normals; rint of an exact power-of-two rescale in the
-// subnormal range. The sign bit is always kept. Every case is computed and
-// the result picked by selects, so a wave never branches per element.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  // below 2^-6 the quantum is 2^-9: rint(|y| * 512) in 0..8 (8 = smallest normal)
-  const float f = __builtin_bit_cast(float, a < 0x3C800000u ? a : 0x3C800000u) * 512.0f;
-  const uint32_t sub = (uint32_t)__builtin_rintf(f);
-  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);   // RNE to 3 mantissa bits
-  const uint32_t nrm = (r >> 20) - (120u << 3);
-  uint32_t c = a < 0x3C800000u ? sub : nrm;
-  c = a >= 0x43E00000u ? 0x7Eu : c;                      // >= 448 (and inf): saturate
-  c = a > 0x7F800000u ? 0x7Fu : c;                       // NaN
-  return s | c;
+// x / s correctly rounded, from r = the correctly rounded 1/s: q = x * r is
+// within an ulp of x / s, the remainder x - s * q is exact under fma, and one
+// correction q + r * (x - s * q) rounded once is the correctly rounded quotient
+// (Markstein's theorem for round-to-nearest, no overflow or underflow in the
+// steps). An exact q (zero remainder, which keeps the sign of a zero x) and a
+// non-finite q (inf x, or a quotient past the fp32 range) are returned as
+// they are. Three operations per element instead of a full division.
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q = x * r;
+  const float e = __builtin_fmaf(-q, s, x);
+  const bool keep = e == 0.0f || !__builtin_isfinite(q);
+  return keep ? q : __builtin_fmaf(e, r, q);
 }
 
-__device__ __forceinline__ uint32_t f32_to_e5m2(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  // below 2^-14 the quantum is 2^-16: rint(|y| * 65536) in 0..4
-  const float f = __builtin_bit_cast(float, a < 0x38800000u ? a : 0x38800000u) * 65536.0f;
-  const uint32_t sub = (uint32_t)__builtin_rintf(f);
-  const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);   // RNE to 2 mantissa bits
-  const uint32_t nrm = (r >> 21) - (112u << 2);
-  uint32_t c = a < 0x38800000u ? sub : nrm;
-  c = a >= 0x47600000u ? 0x7Bu : c;                      // >= 57344 (and inf): saturate
-  c = a > 0x7F800000u ? 0x7Fu : c;                       // NaN
-  return s | c;
+// Four fp32 values -> four FP8 codes (bytes 0..3), round to nearest even,
+// saturating, sign kept, by gfx950's packed conversions. The values are first
+// clamped to the format's largest finite value (NaN passes through), so the
+// result never depends on how the conversion treats overflow.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8x4_from_f32(float y0, float y1, float y2, float y3) {
+  constexpr float kMax = FMT == KV_E4M3 ? 448.0f : 57344.0f;
+  auto sat = [](float y) { return y != y ? y : fminf(fmaxf(y, -kMax), kMax); };
+  y0 = sat(y0); y1 = sat(y1); y2 = sat(y2); y3 = sat(y3);
+  if constexpr (FMT == KV_E4M3) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)lo, true);
+  } else {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(y2, y3, (int)lo, true);
+  }
 }
 
 // 16-bit source element -> fp32 (exact).

@@ -47,6 +47,11 @@ WRITE_CASES = [
     ("e5m2", "bf16", 2048, 64, (3,)),
     ("f16", "f16", 32, 128, (2, 9)),
     ("e4m3", "bf16", 64, 128, (63,)),
+    # head sizes the attention kernels do not take: the 16-dimension write path
+    ("e4m3", "f16", 16, 32, (100, 7)),
+    ("e5m2", "bf16", 64, 256, (70,)),
+    ("e4m3", "bf16", 2048, 256, (130,)),
+    ("f16", "f16", 32, 32, (66,)),
 ]
 
 
@@ -66,30 +71,59 @@ def test_write_bit_exact(runner, fmt, src, bs, D, ctx):
     assert np.array_equal(_cache_np(dc.value_cache).view(np.uint8), vc.view(np.uint8))
 
 
-@pytest.mark.parametrize("fmt,scale", [("e4m3", 1.0), ("e4m3", 0.0105), ("e4m3", 7.0),
-                                       ("e5m2", None), ("e5m2", 0.37)])
-def test_write_every_fp16_pattern(runner, fmt, scale):
-    """All 65536 fp16 bit patterns (NaN and inf included) through the write."""
-    from attention_paged_flashattention_amd import pagedattn as pa
-    log(f"write all fp16 patterns {fmt} scale={scale}")
+WRITE_SCALES = [("e4m3", 1.0), ("e4m3", 0.0105), ("e4m3", 7.0), ("e4m3", 13.0),
+                ("e4m3", 0.2987244725227356), ("e4m3", 3.1415927410125732e-3),
+                ("e5m2", None), ("e5m2", 0.37)]
+
+
+def _all_patterns(src):
+    """Every 16-bit pattern of the source dtype as [512, 1, 128] storage, NaN
+    patterns replaced by 0 (NaN inputs are outside the contract: the sign of a
+    NaN is unspecified)."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    x = bits.view(np.float16).copy()
-    x[np.isnan(x)] = 0          # NaN inputs are outside the contract (sign of NaN unspecified)
-    x = x.reshape(512, 1, 128)
-    T, D, bs = 512, 128, 16
+    if src == "f16":
+        x = bits.view(np.float16).copy()
+        x[np.isnan(x)] = 0
+        return x.reshape(512, 1, 128)
+    f = synth.to_f32(bits, "bf16")
+    bits = bits.copy()
+    bits[np.isnan(f)] = 0
+    return bits.reshape(512, 1, 128)
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("bs,per_call", [(16, 512), (64, 512), (64, 63)])
+@pytest.mark.parametrize("fmt,scale", WRITE_SCALES)
+def test_write_every_16bit_pattern(runner, fmt, scale, bs, per_call, src):
+    """All 65536 fp16 or bf16 bit patterns (inf included) through the write,
+    in calls of 512 tokens (the row kernel; with 64-token pages its
+    contiguous value blocks) or of 63 tokens (the few-token kernel)."""
+    from attention_paged_flashattention_amd import pagedattn as pa
+    log(f"write all {src} patterns {fmt} scale={scale} bs={bs} tokens/call={per_call}")
+    x = _all_patterns(src)
+    T, D = 512, 128
     nb = T // bs
     slots = np.arange(T, dtype=np.int64)
     dev = "cuda:0"
-    k = torch.from_numpy(x.copy()).to(dev)
-    v = torch.from_numpy(x[::-1].copy()).to(dev)
+    if src == "f16":
+        k = torch.from_numpy(x.copy()).to(dev)
+        v = torch.from_numpy(x[::-1].copy()).to(dev)
+    else:
+        k = torch.from_numpy(x.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        v = torch.from_numpy(x[::-1].view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    vg = min(bs, 64)
     kc = torch.full((nb, 1, bs, D), 0x7F, dtype=torch.uint8, device=dev)
-    vc = torch.full((nb, 1, 1, D, bs), 0x7F, dtype=torch.uint8, device=dev)
+    vc = torch.full((nb, 1, bs // vg, D, vg), 0x7F, dtype=torch.uint8, device=dev)
     sc = None if scale is None else torch.tensor([scale], dtype=torch.float32, device=dev)
-    pa.kv_cache_write_fp8(k, v, torch.from_numpy(slots).to(dev), kc, vc, fmt, sc, sc)
+    st = torch.from_numpy(slots).to(dev)
+    for t0 in range(0, T, per_call):
+        t1 = min(T, t0 + per_call)
+        pa.kv_cache_write_fp8(k[t0:t1], v[t0:t1], st[t0:t1], kc, vc, fmt, sc, sc)
     torch.cuda.synchronize()
     okc, ovc = paged.new_caches(nb, 1, bs, D, fmt, fill=0x7F)
     s = None if scale is None else np.array([scale], dtype=np.float32)
-    paged.write(x.astype(np.float32), x[::-1].astype(np.float32), slots, okc, ovc, fmt, s, s)
+    xf = synth.to_f32(x, src)
+    paged.write(xf, xf[::-1].copy(), slots, okc, ovc, fmt, s, s)
     assert np.array_equal(kc.cpu().numpy(), okc)
     assert np.array_equal(vc.cpu().numpy(), ovc)
 
