@@ -132,10 +132,11 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
 
 
-def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=None):
+def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=None, graph=False):
     """Write the newest q_len tokens of every sequence, then decode/verify
     (or the sliding-window attention when ``window`` is set). Returns a result
-    dict with the step time and the split kernel's times."""
+    dict with the step time and the split kernel's times; with ``graph`` also
+    the step time when the same steps are replayed from a captured HIP graph."""
     import torch
     from attention_paged_flashattention_amd import pagedattn as pa
     from attention_paged_flashattention_amd import runner
@@ -199,6 +200,8 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
     step_bytes = kv_bytes + meta + 2 * qo + write_bytes
     split_bytes = kv_bytes + meta + qo
     kern_ms = sum(kern) / len(kern)
+    graph_ms = graph_step_ms(k_new, v_new, s_new, kcs, vcs, c, dc, bind_attn, qv, parts, ws, out,
+                             steps, warmup) if graph else None
     del kcs, vcs, dc
     torch.cuda.empty_cache()
     return dict(name=name, ms_per_step=ms, ms_per_step_with_events=ms_ev, step_bytes=step_bytes,
@@ -206,10 +209,48 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
                 split_us_p10=pct(kern, 10) * 1e3, split_us_p50=pct(kern, 50) * 1e3,
                 split_us_p90=pct(kern, 90) * 1e3,
                 split_ms=kern_ms, split_bytes=split_bytes,
-                split_GBps=split_bytes / kern_ms / 1e6,
+                split_GBps=split_bytes / kern_ms / 1e6, graph_ms_per_step=graph_ms,
                 partitions=(pa.pa_decode_partitions(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
                                                     c.head_dim, dc_max(c)) if window is None else
                             None) if parts == 0 else parts)
+
+
+def graph_step_ms(k_new, v_new, s_new, kcs, vcs, c, dc, bind_attn, qv, parts, ws, out, steps,
+                  warmup):
+    """One graph holds one step (write + attention) per cache copy, captured
+    on a side stream the calls are bound to; replays run back to back and the
+    step time is the replay time over the steps replayed."""
+    import torch
+    from attention_paged_flashattention_amd import pagedattn as pa
+    copies = len(kcs)
+    side = torch.cuda.Stream()
+    calls = []
+    for i in range(copies):
+        calls.append(pa.bind_kv_cache_write_fp8(k_new, v_new, s_new, kcs[i], vcs[i], c.cache_fmt,
+                                                dc.k_scale, dc.v_scale, stream=side))
+        calls.append(bind_attn(qv, kcs[i], vcs[i], c.cache_fmt, dc.block_tables, dc.ctx_lens,
+                               dc.max_ctx, c.softmax_scale, dc.k_scale, dc.v_scale,
+                               num_partitions=parts, workspace=ws, out=out, stream=side)[0])
+    side.wait_stream(torch.cuda.current_stream())
+    for f in calls:                   # eager warm-up on the side stream
+        f()
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    for _ in range(max(1, warmup // copies)):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / (reps * copies)
+    del g
+    return ms
 
 
 def dc_max(c):
@@ -483,7 +524,7 @@ def main():
     if "decode128k" in sections:
         log("section decode128k")
         res["decode128k"] = decode_like_section(ev, synth.headline_decode_128k(), K, W, 4, 1,
-                                                "decode_128k_e4m3_bs2048_p64")
+                                                "decode_128k_e4m3_bs2048_p64", graph=True)
     if "prefill32k" in sections:
         log("section prefill32k")
         res["prefill32k"] = prefill_section(ev, synth.chunked_prefill_32k(), max(10, K // 5),
@@ -541,6 +582,12 @@ def main():
     if h:
         line.update(value=round(h["GBps"], 1), unit="GB/s", ms_per_step=round(h["ms_per_step"], 5),
                     ms_per_step_with_kernel_events=round(h["ms_per_step_with_events"], 5))
+        if h["graph_ms_per_step"]:
+            line["decode_128k_graph_replay"] = {
+                "ms_per_step": round(h["graph_ms_per_step"], 5),
+                "GBps": round(h["step_bytes"] / h["graph_ms_per_step"] / 1e6, 1),
+                "frac_of_hbm_peak": round(h["step_bytes"] / h["graph_ms_per_step"] / 1e6
+                                          / HBM_PEAK_GBPS, 4)}
         line["dtype"] = "fp16"
         line["config"] = {"workload": h["name"], "batch": 1, "context": 131072,
                           "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
