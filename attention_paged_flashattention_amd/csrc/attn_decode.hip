@@ -78,6 +78,9 @@ __device__ __forceinline__ half8 val_op(const uint32_t* dw) {
 }
 
 constexpr float kNegInf = -__builtin_inff();
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 // Growth of the running max (log2 units) tolerated before O and l are rescaled.
 constexpr float kRescaleSlackD = 8.0f;
 
@@ -99,6 +102,57 @@ struct TilePages {
 
 __device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Fused quantize-on-write: new tokens i0 .. i1-1 of sequence b (positions
+// p0 + i) for KV head g, written into the caches with the same encoding as the
+// write kernels (a 16-byte source chunk -> 8 codes per thread and task). Each
+// key row chunk is one 8-byte store (16 for fp16); the 8 value codes of a chunk
+// go to 8 dimension rows of the token's value group.
+template <int D, int FMT, int QT>
+__device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, int b, int g, int p0,
+                                                  int i0, int i1, const int32_t* btb) {
+  constexpr int ES = (FMT == KV_F16) ? 2 : 1;
+  constexpr int CH = D / 8;                   // 16-byte source chunks per row
+  const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
+  const float kdiv = ksc ? a.k_scale[g] : 1.0f;
+  const float vdiv = vsc ? a.v_scale[g] : 1.0f;
+  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
+  const int bs_log2 = a.bs_log2;
+  const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
+  const int64_t T = (int64_t)1 << vg_log2;
+  const int tasks = (i1 - i0) * 2 * CH;
+  for (int e = threadIdx.x; e < tasks; e += 256) {
+    const int i = i0 + e / (2 * CH);
+    const int r = e % (2 * CH);
+    const bool isv = r >= CH;
+    const int ch = isv ? r - CH : r;
+    const int pos = p0 + i;
+    const uint16_t* src = (isv ? a.v_new : a.k_new) +
+                          ((int64_t)(b * a.q_len + i) * a.num_kv_heads + g) * D + ch * 8;
+    const u32x4 w = ld16(src);
+    const int64_t page = btb[pos >> bs_log2];
+    const int64_t off = pos & ((1 << bs_log2) - 1);
+    const int64_t ph = page * a.num_kv_heads + g;
+    const u32x4 codes = isv ? encode8<QT, FMT>(w, vsc, vdiv, vrcp)
+                            : encode8<QT, FMT>(w, ksc, kdiv, krcp);
+    if (!isv) {
+      uint8_t* kdst = a.key_cache_w + (((ph << bs_log2) + off) * D + ch * 8) * ES;
+      if constexpr (ES == 2) *reinterpret_cast<u32x4*>(kdst) = codes;
+      else *reinterpret_cast<u32x2*>(kdst) = u32x2{codes.x, codes.y};
+    } else {
+      uint8_t* vdst = a.value_cache_w +
+          ((((ph << (bs_log2 - vg_log2)) + (off >> vg_log2)) * D + ch * 8) * T + (off & (T - 1))) * ES;
+      const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if constexpr (ES == 2)
+          reinterpret_cast<uint16_t*>(vdst)[(int64_t)k * T] = (uint16_t)(cw[k >> 1] >> ((k & 1) * 16));
+        else
+          vdst[(int64_t)k * T] = (uint8_t)(cw[k >> 2] >> ((k & 3) * 8));
+      }
+    }
+  }
 }
 
 // UNI: block_size >= 64, so every 64-key tile lies in one page and its page id
@@ -209,6 +263,21 @@ void decode_split_kernel(const DecodeArgs a) {
   };
 
   const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
+
+  // Fused quantize-on-write: the work-group whose keys hold some of the new
+  // tokens writes them for its KV head before any load (no other work-group
+  // reads those keys of this head). Each wave waits until its stores have
+  // reached the L2 (vmcnt 0: gfx9 counts stores there too), then the barrier
+  // orders them before every wave's loads of those keys.
+  if (a.k_new != nullptr) {
+    const int p0 = ctx - a.q_len;   // position of new token 0
+    const int i0 = max(0, tb - p0), i1 = min(a.q_len, te - p0);
+    if (i1 > i0) {
+      append_new_tokens<D, FMT, QT>(a, b, g, p0, i0, i1, btb);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
+  }
 
   // Start the first tile's traffic before anything else.
   Tile A, B;

@@ -23,25 +23,6 @@
 
 namespace pa {
 
-// 8 source elements (one 16-byte chunk) -> 8 cache codes: FP8 in the low 8
-// bytes, or the fp16 elements unchanged.
-template <int ST, int FMT>
-__device__ __forceinline__ u32x4 encode8(u32x4 w, bool scaled, float div, float rdiv) {
-  if constexpr (FMT == KV_F16) {
-    return w;
-  } else {
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = src_to_f32<ST>((uint16_t)(ww[i >> 1] >> ((i & 1) * 16)));
-      y[i] = scaled ? div_rn(x, div, rdiv) : x;   // x / div, correctly rounded
-    }
-    return u32x4{fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]),
-                 fp8x4_from_f32<FMT>(y[4], y[5], y[6], y[7]), 0u, 0u};
-  }
-}
-
 // 4 source elements (8 bytes) -> 4 FP8 codes.
 template <int ST, int FMT>
 __device__ __forceinline__ uint32_t encode4(u32x2 w, bool scaled, float div, float rdiv) {

@@ -41,6 +41,13 @@ struct DecodeArgs {
   int num_parts;
   int window;               // -1: causal rows; W >= 0: non-causal window of W keys
   float softmax_scale;
+  // Fused quantize-on-write (null k_new: none): the q_len new tokens of each
+  // sequence, [batch][q_len][Hkv][D] in the query dtype, are written at their
+  // positions ctx - q_len + i before they are attended.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* key_cache_w;     // the caches above, for the fused write
+  uint8_t* value_cache_w;
 };
 
 struct PrefillArgs {

@@ -164,7 +164,7 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
                       int head_dim, const float* k_scale, const float* v_scale,
                       float softmax_scale, int num_partitions, void* workspace,
                       size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream,
-                      int window = -1) {
+                      int window = -1, const void* k_new = nullptr, const void* v_new = nullptr) {
   if (batch < 0) return fail(PA_ERR_INVALID_ARG, "%s: batch must be >= 0", name);
   if (q_len <= 0) return fail(PA_ERR_INVALID_ARG, "%s: q_len must be positive", name);
   if (num_partitions < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_partitions must be >= 0", name);
@@ -214,6 +214,10 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
   a.num_parts = parts;
   a.window = window < 0 ? -1 : std::min(window, max_context_len);
   a.softmax_scale = softmax_scale;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.key_cache_w = k_new ? static_cast<uint8_t*>(const_cast<void*>(kc)) : nullptr;
+  a.value_cache_w = k_new ? static_cast<uint8_t*>(const_cast<void*>(vc)) : nullptr;
   const int nrows = q_len * G;
   const int nqb = nrows <= 16 ? 1 : (nrows <= 32 ? 2 : 4);
   hipError_t e = pa::launch_decode(a, batch, head_dim, cache_fmt(cache_dtype), q_type(q_dtype),
@@ -393,6 +397,27 @@ PA_API pa_status attn_window_paged(const void* q, pa_dtype q_dtype, int batch, i
                      context_lens, max_context_len, num_q_heads, num_kv_heads, head_dim, k_scale,
                      v_scale, softmax_scale, num_partitions, workspace, workspace_bytes, out,
                      out_dtype, stream, window_left);
+}
+
+PA_API pa_status attn_decode_append_paged(const void* q, pa_dtype q_dtype, int batch, int q_len,
+                                          const void* key_new, const void* value_new,
+                                          void* key_cache, void* value_cache,
+                                          pa_dtype cache_dtype, int block_size,
+                                          int64_t num_blocks, const int32_t* block_tables,
+                                          int max_blocks_per_seq, const int32_t* context_lens,
+                                          int max_context_len, int num_q_heads, int num_kv_heads,
+                                          int head_dim, const float* k_scale,
+                                          const float* v_scale, float softmax_scale,
+                                          int num_partitions, void* workspace,
+                                          size_t workspace_bytes, void* out, pa_dtype out_dtype,
+                                          void* stream) {
+  if (!key_new || !value_new)
+    return fail(PA_ERR_INVALID_ARG, "attn_decode_append_paged: null key_new or value_new");
+  return decode_like("attn_decode_append_paged", q, q_dtype, batch, q_len, key_cache, value_cache,
+                     cache_dtype, block_size, num_blocks, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_q_heads, num_kv_heads, head_dim, k_scale,
+                     v_scale, softmax_scale, num_partitions, workspace, workspace_bytes, out,
+                     out_dtype, stream, -1, key_new, value_new);
 }
 
 PA_API int pa_decode_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads,

@@ -25,7 +25,8 @@ CACHE_DTYPES = {"f16": PA_F16, "e4m3": PA_FP8_E4M3, "e5m2": PA_FP8_E5M2}
 TORCH_DTYPES = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float32: PA_F32}
 
 EXPORTS = ["kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
-           "attn_verify_paged", "attn_window_paged", "pa_window_workspace_bytes",
+           "attn_verify_paged", "attn_decode_append_paged", "attn_window_paged",
+           "pa_window_workspace_bytes",
            "pa_decode_partitions", "pa_workspace_bytes",
            "pa_supports", "pa_last_error", "pa_version", "pa_validate_tables",
            "pa_profile_next_call"]
@@ -56,6 +57,7 @@ _DECODE_TAIL = [_vp, _vp, _i32, _i32, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _i
 _lib.attn_decode_paged.argtypes = [_vp, _i32, _i32] + _DECODE_TAIL
 _lib.attn_verify_paged.argtypes = [_vp, _i32, _i32, _i32] + _DECODE_TAIL
 _lib.attn_window_paged.argtypes = [_vp, _i32, _i32, _i32, _i32] + _DECODE_TAIL
+_lib.attn_decode_append_paged.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp] + _DECODE_TAIL
 _lib.pa_window_workspace_bytes.argtypes = [_i32] * 8
 _lib.pa_window_workspace_bytes.restype = _sz
 _lib.pa_decode_partitions.argtypes = [_i32] * 6
@@ -70,7 +72,8 @@ _lib.pa_validate_tables.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i64, _vp]
 _lib.pa_profile_next_call.argtypes = [_vp, _vp]
 _lib.pa_profile_next_call.restype = None
 for _name in ("kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
-              "attn_verify_paged", "attn_window_paged", "pa_validate_tables"):
+              "attn_verify_paged", "attn_decode_append_paged", "attn_window_paged",
+              "pa_validate_tables"):
     getattr(_lib, _name).restype = _i32
 
 
@@ -233,7 +236,7 @@ def pa_supports(op, q_dtype, cache_dtype, head_dim, num_q_heads, num_kv_heads, b
 
 def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_tables, context_lens,
                  max_context_len, softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
-                 out_dtype, stream, bind=False, window=None):
+                 out_dtype, stream, bind=False, window=None, new_kv=None):
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
     batch = q.shape[0]
@@ -252,7 +255,17 @@ def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_ta
             _ptr(k_scale), _ptr(v_scale), float(softmax_scale), int(num_partitions),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
             TORCH_DTYPES[out.dtype], _stream(q.device, stream)]
-    if op == PA_OP_DECODE:
+    keep = ()
+    if new_kv is not None:
+        k_new, v_new = new_kv
+        shape = (batch, q_len, hkv, d)
+        for t, name in ((k_new, "key_new"), (v_new, "value_new")):
+            _need(t, name, q.dtype)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        args = [_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len, _ptr(k_new), _ptr(v_new)] + args
+        keep = (k_new, v_new)
+    elif op == PA_OP_DECODE:
         args = [_ptr(q), TORCH_DTYPES[q.dtype], batch] + args
     elif op == PA_OP_WINDOW:
         args = [_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len, int(window)] + args
@@ -260,7 +273,7 @@ def _decode_like(fn, op, q, q_len, key_cache, value_cache, cache_dtype, block_ta
         args = [_ptr(q), TORCH_DTYPES[q.dtype], batch, q_len] + args
     if bind:
         return Bound(fn, args, (q, key_cache, value_cache, block_tables, context_lens, k_scale,
-                                v_scale, workspace, out)), out
+                                v_scale, workspace, out) + keep), out
     _check(fn(*args))
     return out
 
@@ -306,6 +319,32 @@ def attn_verify_paged(q, key_cache, value_cache, cache_dtype, block_tables, cont
                         value_cache, cache_dtype, block_tables, context_lens, max_context_len,
                         softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
                         out_dtype, stream)
+
+
+def attn_decode_append_paged(q, key_new, value_new, key_cache, value_cache, cache_dtype,
+                             block_tables, context_lens, max_context_len, softmax_scale,
+                             k_scale=None, v_scale=None, num_partitions=0, workspace=None,
+                             out=None, out_dtype=None, stream=None):
+    """q [B, q_len, Hq, D]; key_new, value_new [B, q_len, Hkv, D] (q's dtype)
+    -> out [B, q_len, Hq, D]. Writes the new tokens at positions
+    ctx_b - q_len .. ctx_b - 1 of each sequence's pages, then attends (one
+    kernel for both)."""
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    return _decode_like(_lib.attn_decode_append_paged, PA_OP_VERIFY, q, q.shape[1], key_cache,
+                        value_cache, cache_dtype, block_tables, context_lens, max_context_len,
+                        softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
+                        out_dtype, stream, new_kv=(key_new, value_new))
+
+
+def bind_attn_decode_append_paged(q, key_new, value_new, key_cache, value_cache, cache_dtype,
+                                  block_tables, context_lens, max_context_len, softmax_scale,
+                                  k_scale=None, v_scale=None, num_partitions=0, workspace=None,
+                                  out=None, out_dtype=None, stream=None):
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    return _decode_like(_lib.attn_decode_append_paged, PA_OP_VERIFY, q, q.shape[1], key_cache,
+                        value_cache, cache_dtype, block_tables, context_lens, max_context_len,
+                        softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
+                        out_dtype, stream, bind=True, new_kv=(key_new, value_new))
 
 
 def attn_window_paged(q, window_left, key_cache, value_cache, cache_dtype, block_tables,

@@ -132,11 +132,13 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
 
 
-def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=None, graph=False):
+def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=None, graph=False,
+                        fused=False):
     """Write the newest q_len tokens of every sequence, then decode/verify
-    (or the sliding-window attention when ``window`` is set). Returns a result
-    dict with the step time and the split kernel's times; with ``graph`` also
-    the step time when the same steps are replayed from a captured HIP graph."""
+    (or the sliding-window attention when ``window`` is set). With ``fused``
+    the two are one call (attn_decode_append_paged). Returns a result dict with
+    the step time and the split kernel's times; with ``graph`` also the step
+    time when the same steps are replayed from a captured HIP graph."""
     import torch
     from attention_paged_flashattention_amd import pagedattn as pa
     from attention_paged_flashattention_amd import runner
@@ -148,6 +150,7 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
     newest = dc.last_token_rows(q_len)
     k_new, v_new, s_new = dc.k[newest].contiguous(), dc.v[newest].contiguous(), dc.slots[newest].contiguous()
     c = case
+    assert not fused or (window is None and len(newest) == c.batch * q_len)
     parts = c.meta.get("partitions", 0)
     if window is not None:
         wsb = pa.pa_window_workspace_bytes(c.batch, q_len, c.num_q_heads, c.num_kv_heads,
@@ -157,29 +160,44 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
         wsb = pa.pa_workspace_bytes(op, c.batch, q_len, c.num_q_heads, c.num_kv_heads,
                                     c.head_dim, parts, dc.max_ctx)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dc.device)
-    qv = dc.q if (q_len == 1 and window is None) else dc.q.view(c.batch, q_len, c.num_q_heads,
-                                                                 c.head_dim)
+    q4 = dc.q.view(c.batch, q_len, c.num_q_heads, c.head_dim)
+    qv = dc.q if (q_len == 1 and window is None and not fused) else q4
     out = torch.empty_like(qv)
     starts = [ev.create() for _ in range(steps)]
     stops = [ev.create() for _ in range(steps)]
-    if window is not None:
-        def bind_attn(*args, **kw):
-            return pa.bind_attn_window_paged(args[0], window, *args[1:], **kw)
-    else:
-        bind_attn = pa.bind_attn_decode_paged if q_len == 1 else pa.bind_attn_verify_paged
-    # arguments marshalled once per cache copy: the timed loop only issues calls
-    writes = [pa.bind_kv_cache_write_fp8(k_new, v_new, s_new, kcs[i], vcs[i], c.cache_fmt,
-                                         dc.k_scale, dc.v_scale) for i in range(copies)]
-    attns = [bind_attn(qv, kcs[i], vcs[i], c.cache_fmt, dc.block_tables, dc.ctx_lens, dc.max_ctx,
-                       c.softmax_scale, dc.k_scale, dc.v_scale, num_partitions=parts,
-                       workspace=ws, out=out)[0] for i in range(copies)]
+    new_shape = (c.batch, q_len, c.num_kv_heads, c.head_dim)
+
+    def step_calls(i, stream=None):
+        """The bound calls of one step on cache copy i (marshalled once: the
+        timed loops only issue calls)."""
+        common = dict(num_partitions=parts, workspace=ws, out=out, stream=stream)
+        if fused:
+            return [pa.bind_attn_decode_append_paged(
+                q4, k_new.view(new_shape), v_new.view(new_shape), kcs[i], vcs[i], c.cache_fmt,
+                dc.block_tables, dc.ctx_lens, dc.max_ctx, c.softmax_scale, dc.k_scale,
+                dc.v_scale, **common)[0]]
+        w = pa.bind_kv_cache_write_fp8(k_new, v_new, s_new, kcs[i], vcs[i], c.cache_fmt,
+                                       dc.k_scale, dc.v_scale, stream=stream)
+        args = (qv, kcs[i], vcs[i], c.cache_fmt, dc.block_tables, dc.ctx_lens, dc.max_ctx,
+                c.softmax_scale, dc.k_scale, dc.v_scale)
+        if window is not None:
+            a = pa.bind_attn_window_paged(args[0], window, *args[1:], **common)[0]
+        elif q_len == 1:
+            a = pa.bind_attn_decode_paged(*args, **common)[0]
+        else:
+            a = pa.bind_attn_verify_paged(*args, **common)[0]
+        return [w, a]
+
+    calls = [step_calls(i) for i in range(copies)]
     torch.cuda.synchronize()
 
     def step(i, record):
-        writes[i % copies]()
+        cs = calls[i % copies]
+        for f in cs[:-1]:
+            f()
         if record:
             pa.pa_profile_next_call(starts[i], stops[i])
-        attns[i % copies]()
+        cs[-1]()
 
     # the step rate from a loop with no events; the split kernel's launch
     # durations from a second timed loop of the same steps with an event pair
@@ -198,11 +216,17 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
     newest_n = len(newest)
     write_bytes = newest_n * c.num_kv_heads * c.head_dim * (2 * 2 + 2) + newest_n * 8
     step_bytes = kv_bytes + meta + 2 * qo + write_bytes
-    split_bytes = kv_bytes + meta + qo
+    # the fused kernel also reads the new tokens and writes their codes (no
+    # slot array: slots come from the block table it reads anyway)
+    fused_write = newest_n * c.num_kv_heads * c.head_dim * (2 * 2 + 2)
+    split_bytes = kv_bytes + meta + qo + (fused_write if fused else 0)
     kern_ms = sum(kern) / len(kern)
-    graph_ms = graph_step_ms(k_new, v_new, s_new, kcs, vcs, c, dc, bind_attn, qv, parts, ws, out,
-                             steps, warmup) if graph else None
-    del kcs, vcs, dc
+    graph_ms = None
+    if graph:
+        side = torch.cuda.Stream()
+        graph_ms = graph_step_ms([f for i in range(copies) for f in step_calls(i, side)], side,
+                                 copies, steps, warmup)
+    del kcs, vcs, dc, calls
     torch.cuda.empty_cache()
     return dict(name=name, ms_per_step=ms, ms_per_step_with_events=ms_ev, step_bytes=step_bytes,
                 GBps=step_bytes / ms / 1e6,
@@ -215,22 +239,11 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
                             None) if parts == 0 else parts)
 
 
-def graph_step_ms(k_new, v_new, s_new, kcs, vcs, c, dc, bind_attn, qv, parts, ws, out, steps,
-                  warmup):
-    """One graph holds one step (write + attention) per cache copy, captured
-    on a side stream the calls are bound to; replays run back to back and the
-    step time is the replay time over the steps replayed."""
+def graph_step_ms(calls, side, copies, steps, warmup):
+    """One graph holds the calls of one step per cache copy, captured on the
+    side stream they are bound to; replays run back to back and the step time
+    is the replay time over the steps replayed."""
     import torch
-    from attention_paged_flashattention_amd import pagedattn as pa
-    copies = len(kcs)
-    side = torch.cuda.Stream()
-    calls = []
-    for i in range(copies):
-        calls.append(pa.bind_kv_cache_write_fp8(k_new, v_new, s_new, kcs[i], vcs[i], c.cache_fmt,
-                                                dc.k_scale, dc.v_scale, stream=side))
-        calls.append(bind_attn(qv, kcs[i], vcs[i], c.cache_fmt, dc.block_tables, dc.ctx_lens,
-                               dc.max_ctx, c.softmax_scale, dc.k_scale, dc.v_scale,
-                               num_partitions=parts, workspace=ws, out=out, stream=side)[0])
     side.wait_stream(torch.cuda.current_stream())
     for f in calls:                   # eager warm-up on the side stream
         f()
@@ -524,7 +537,11 @@ def main():
     if "decode128k" in sections:
         log("section decode128k")
         res["decode128k"] = decode_like_section(ev, synth.headline_decode_128k(), K, W, 4, 1,
-                                                "decode_128k_e4m3_bs2048_p64", graph=True)
+                                                "decode_128k_e4m3_bs2048_p64", graph=True,
+                                                fused=True)
+        log("section decode128k, write and decode as two calls")
+        res["decode128k_2call"] = decode_like_section(ev, synth.headline_decode_128k(), K, W, 4, 1,
+                                                      "decode_128k_e4m3_bs2048_p64", graph=True)
     if "prefill32k" in sections:
         log("section prefill32k")
         res["prefill32k"] = prefill_section(ev, synth.chunked_prefill_32k(), max(10, K // 5),
@@ -533,6 +550,8 @@ def main():
         log("section verify128k")
         res["verify128k"] = decode_like_section(ev, synth.verify_q8_128k(), K, W, 1, 8,
                                                 "verify_q8_b4_128k_e5m2_bs2048")
+        res["verify128k_fused"] = decode_like_section(ev, synth.verify_q8_128k(), K, W, 1, 8,
+                                                      "verify_q8_b4_128k_e5m2_bs2048", fused=True)
     if "verify_q16" in sections:
         log("section verify_q16")
         res["verify_q16"] = decode_like_section(ev, synth.verify_q16_128k(), K, W, 1, 16,
@@ -588,11 +607,22 @@ def main():
                 "GBps": round(h["step_bytes"] / h["graph_ms_per_step"] / 1e6, 1),
                 "frac_of_hbm_peak": round(h["step_bytes"] / h["graph_ms_per_step"] / 1e6
                                           / HBM_PEAK_GBPS, 4)}
+        h2 = res.get("decode128k_2call")
+        if h2:
+            line["decode_128k_two_calls"] = {
+                "what": "kv_cache_write_fp8 + attn_decode_paged (write kernel, split, combine)",
+                "GBps": round(h2["GBps"], 1), "us_per_step": round(h2["ms_per_step"] * 1e3, 2),
+                "frac_of_hbm_peak": round(h2["GBps"] / HBM_PEAK_GBPS, 4),
+                "split_kernel_us": round(h2["split_ms"] * 1e3, 2),
+                "graph_replay_us_per_step": round(h2["graph_ms_per_step"] * 1e3, 2)
+                if h2["graph_ms_per_step"] else None}
         line["dtype"] = "fp16"
         line["config"] = {"workload": h["name"], "batch": 1, "context": 131072,
                           "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
                           "block_size": 2048, "kv_cache": "fp8_e4m3 per-head scales",
-                          "partitions": h["partitions"], "cache_copies_rotated": 4}
+                          "partitions": h["partitions"], "cache_copies_rotated": 4,
+                          "step": "attn_decode_append_paged: quantize-on-write of the new "
+                                  "token fused into the split kernel, then the combine"}
         ach = h["split_GBps"]
         tr = counters("decode_split_128k_e4m3", dec_sha)
         line["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel",
@@ -627,7 +657,9 @@ def main():
                                     "traffic": trp,
                                     "algorithmic_flops_per_step": p["flops"],
                                     "avg_launch_us": round(p["kernel_ms"] / p["launches_per_step"] * 1e3, 1)}
-    for key, out_key in [("verify128k", "verify_q8_128k"), ("verify_q16", "verify_q16_128k"),
+    for key, out_key in [("verify128k", "verify_q8_128k"),
+                         ("verify128k_fused", "verify_q8_128k_fused_write"),
+                         ("verify_q16", "verify_q16_128k"),
                          ("decode256k", "decode_256k"), ("decode_b8", "decode_b8"),
                          ("decode_b16", "decode_b16_16k_e5m2")]:
         r = res.get(key)

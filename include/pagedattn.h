@@ -12,7 +12,9 @@
  *                          plus a log-sum-exp combine (long-context decode);
  *   attn_verify_paged   -- the grouped speculative-verify step: q_len new
  *                          causal tokens per sequence (q_len = 8 is the q8
- *                          verifier: seven drafts plus one).
+ *                          verifier: seven drafts plus one);
+ *   attn_decode_append_paged -- decode / verify with the new tokens'
+ *                          quantize-on-write fused into the same kernel.
  *
  * Semantics shared by the attention calls. Sequence b has context_lens[b]
  * keys, counting its new tokens (which must already be in the cache: write,
@@ -189,6 +191,43 @@ PA_API pa_status attn_decode_paged(
 PA_API pa_status attn_verify_paged(
     const void* q, pa_dtype q_dtype, int batch, int q_len,
     const void* key_cache, const void* value_cache, pa_dtype cache_dtype,
+    int block_size, int64_t num_blocks,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int max_context_len,
+    int num_q_heads, int num_kv_heads, int head_dim,
+    const float* k_scale, const float* v_scale, float softmax_scale,
+    int num_partitions, void* workspace, size_t workspace_bytes,
+    void* out, pa_dtype out_dtype, void* stream);
+
+/*
+ * Write-then-attend in one call: the quantize-on-write of the q_len newest
+ * tokens of every sequence fused into the decode / verify kernel. The pages
+ * write each step's new K/V into the FP8 cache ("1Cat-vLLM 1.0.0" README,
+ * "Optional experimental feature: FP8 KV cache") and then attend over it
+ * (decode, or the grouped q8 verify of the 1.5.0 notes); here the work-group
+ * that will read a new token's keys writes them first, which saves the write
+ * kernel's launch and its round trip through HBM of a one-token step.
+ *
+ * Result (cache bytes and out) identical to
+ *     kv_cache_write_fp8(key_new, value_new, q_dtype, slots, batch * q_len, ...)
+ *     attn_verify_paged(q, ..., q_len, ...)      (attn_decode_paged if q_len = 1)
+ * with slots[b * q_len + i] = block_tables[b][pos / block_size] * block_size
+ * + pos % block_size at pos = context_lens[b] - q_len + i, i.e. each new token
+ * goes to its own position in the sequence's pages (tokens with pos < 0 are
+ * not written). The encoding is the one of kv_cache_write_fp8, bit for bit.
+ *
+ *   key_new, value_new  [batch][q_len][num_kv_heads][head_dim], in q_dtype
+ *                       (the write's source dtype)
+ *   key_cache, value_cache  written at the new tokens' slots only
+ * Other arguments as in attn_verify_paged (workspace op PA_OP_VERIFY). The
+ * pages holding the new tokens must not be read by another sequence of the
+ * same call (a shared prefix page is fine; the page being appended to is the
+ * sequence's own).
+ */
+PA_API pa_status attn_decode_append_paged(
+    const void* q, pa_dtype q_dtype, int batch, int q_len,
+    const void* key_new, const void* value_new,
+    void* key_cache, void* value_cache, pa_dtype cache_dtype,
     int block_size, int64_t num_blocks,
     const int32_t* block_tables, int max_blocks_per_seq,
     const int32_t* context_lens, int max_context_len,

@@ -253,3 +253,35 @@ def test_supports_window(pa):
     assert pa.pa_supports(pa.PA_OP_WINDOW, 0, 4, 128, 32, 8, 2048, 8)
     assert pa.pa_supports(pa.PA_OP_WINDOW, 0, 3, 128, 32, 8, 16, 16)
     assert not pa.pa_supports(pa.PA_OP_WINDOW, 0, 3, 128, 32, 8, 16, 17)
+
+
+def _call_append(pa, q_len, knew=FAKE, vnew=FAKE, **kw):
+    a = _decode_args(**kw)
+    return pa.lib().attn_decode_append_paged(a["q"], a["q_dtype"], a["batch"], q_len, knew, vnew,
+                                             a["kc"], a["vc"], a["cache_dtype"], a["bs"], a["nb"],
+                                             a["bt"], a["maxblk"], a["ctx"], a["maxctx"], a["hq"],
+                                             a["hkv"], a["d"], a["ks"], a["vs"], a["scale"],
+                                             a["parts"], a["ws"], a["wsb"], a["out"],
+                                             a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("q_len,kw,status", [
+    (1, dict(knew=NUL), 1),
+    (8, dict(vnew=NUL), 1),
+    (1, dict(q=NUL), 1),
+    (0, {}, 1),                           # q_len must be positive
+    (17, {}, 2),                          # 17 * G(4) rows exceed one group
+    (1, dict(d=96), 2),
+    (1, dict(cache_dtype=0, q_dtype=1), 2),   # an fp16 cache takes fp16 sources
+    (8, dict(ks=NUL), 1),                 # E4M3 needs scales for the write too
+    (1, dict(wsb=16), 1),
+    (8, dict(maxctx=65), 1),
+])
+def test_append_rejects_before_launch(pa, q_len, kw, status):
+    assert _call_append(pa, q_len, **kw) == status
+    assert pa.pa_last_error() != ""
+
+
+def test_append_batch_zero_is_a_noop(pa):
+    assert _call_append(pa, 8, batch=0) == 0
+    assert pa.pa_last_error() == ""
