@@ -166,7 +166,9 @@ struct DecodePipe {
   static constexpr bool value = FMT != KV_F16 && NQB == 1;
 };
 
-template <int D, int FMT, int QT, int NQB, bool UNI>
+// APPEND: the fused quantize-on-write of the new tokens (a separate
+// instantiation, so the plain decode / verify kernels carry none of its code).
+template <int D, int FMT, int QT, int NQB, bool UNI, bool APPEND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodePipe<FMT, NQB>::value ? 2 : 1)))
 void decode_split_kernel(const DecodeArgs a) {
   constexpr bool PIPE = DecodePipe<FMT, NQB>::value;
@@ -269,7 +271,7 @@ void decode_split_kernel(const DecodeArgs a) {
   // reads those keys of this head). Each wave waits until its stores have
   // reached the L2 (vmcnt 0: gfx9 counts stores there too), then the barrier
   // orders them before every wave's loads of those keys.
-  if (a.k_new != nullptr) {
+  if constexpr (APPEND) {
     const int p0 = ctx - a.q_len;   // position of new token 0
     const int i0 = max(0, tb - p0), i1 = min(a.q_len, te - p0);
     if (i1 > i0) {
@@ -573,13 +575,21 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   }
 }
 
-template <int D, int FMT, int QT, int NQB>
-static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
+template <int D, int FMT, int QT, int NQB, bool APPEND>
+static void launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream) {
   dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
   if (a.bs_log2 >= 6)
-    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, true, APPEND>), grid, dim3(256), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, false, APPEND>), grid, dim3(256), 0,
+                       stream, a);
+}
+
+template <int D, int FMT, int QT, int NQB>
+static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
+  if (a.k_new != nullptr) launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream);
+  else launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream);
 }
 
 template <int D, int FMT, int QT>

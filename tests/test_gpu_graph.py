@@ -151,3 +151,57 @@ def test_prefill_chunk_graph(runner):
         return torch.randn(q.shape, generator=gen).to(q.dtype).to(q.device)
 
     _replay_and_compare(g, q, out_g, lambda: call(out_e), fresh_q)
+
+
+@pytest.mark.parametrize("fmt,q_len,ctx,bs", [("e4m3", 1, (3000, 5000), 2048),
+                                             ("e5m2", 8, (200, 4100), 64)])
+def test_fused_append_step_graph(runner, fmt, q_len, ctx, bs):
+    """The write-then-attend step as one call (attn_decode_append_paged)
+    captured and replayed: the capture's own run and every replay rewrite the
+    newest slots from the captured new-token buffers, so a replay after the
+    slots were poisoned must restore them and match the oracle."""
+    from attention_paged_flashattention_amd import pagedattn as pa
+    log(f"graph fused {fmt} q_len={q_len} ctx={ctx} bs={bs}")
+    B = len(ctx)
+    case = synth.make_case(f"graph-fused-{fmt}-q{q_len}", 23, list(ctx), q_len, 32, 8, 128, bs,
+                           "f16", "f16", fmt, sigma_kv=0.5)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    newest = dc.last_token_rows(q_len)
+    shape = (B, q_len, 8, 128)
+    k_new = dc.k[newest].contiguous().view(shape)
+    v_new = dc.v[newest].contiguous().view(shape)
+    kc_ref, vc_ref = dc.key_cache.clone(), dc.value_cache.clone()
+    wsb = pa.pa_workspace_bytes(pa.PA_OP_VERIFY, B, q_len, 32, 8, 128, 0, dc.max_ctx)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dc.device)
+    q = dc.q.view(B, q_len, 32, 128).clone()
+    out_g = torch.empty(q.shape, dtype=torch.float32, device=dc.device)
+    out_e = torch.empty_like(out_g)
+
+    def call(out):
+        return pa.attn_decode_append_paged(q, k_new, v_new, dc.key_cache, dc.value_cache, fmt,
+                                           dc.block_tables, dc.ctx_lens, dc.max_ctx,
+                                           case.softmax_scale, dc.k_scale, dc.v_scale,
+                                           workspace=ws, out=out)
+
+    g = _capture(lambda: call(out_g))
+    # poison the newest slots: the replay's fused write must put them back
+    for b in range(B):
+        for i in range(q_len):
+            pos = int(case.ctx_lens[b]) - q_len + i
+            page = int(case.block_tables[b, pos // bs])
+            off = pos % bs
+            dc.key_cache[page, :, off, :] = synth.POISON[fmt]
+            dc.value_cache[page, :, off // min(bs, 64), :, off % min(bs, 64)] = synth.POISON[fmt]
+    out_g.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(dc.key_cache, kc_ref) and torch.equal(dc.value_cache, vc_ref)
+    ref = oracle_full(case)
+    check_close(out_g.reshape(ref.shape), ref, fmt, "fused graph replay vs oracle")
+    gen = torch.Generator(device="cpu").manual_seed(7)
+
+    def fresh_q(r):
+        return torch.randn(q.shape, generator=gen).to(q.dtype).to(q.device)
+
+    _replay_and_compare(g, q, out_g, lambda: call(out_e), fresh_q)
