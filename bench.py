@@ -370,9 +370,14 @@ def small_section(ev, steps):
     qd = dc.q[64:65].contiguous()
     dec = pa.bind_attn_decode_paged(qd, dc.key_cache, dc.value_cache, "f16", dc.block_tables,
                                     ctx65, 65, case.softmax_scale)[0]
+    fdec = pa.bind_attn_decode_append_paged(qd.view(1, 1, 4, 64), dc.k[64:65].view(1, 1, 1, 64),
+                                            dc.v[64:65].view(1, 1, 1, 64), dc.key_cache,
+                                            dc.value_cache, "f16", dc.block_tables, ctx65, 65,
+                                            case.softmax_scale)[0]
     stream = torch.cuda.current_stream().cuda_stream
     res = {}
-    for name, calls in (("prefill64_us", (wpf, pf)), ("decode_at_64_us", (wdec, dec))):
+    for name, calls in (("prefill64_us", (wpf, pf)), ("decode_at_64_us", (wdec, dec)),
+                        ("decode_at_64_fused_write_us", (fdec,))):
         evs = [(ev.create(), ev.create()) for _ in range(steps)]
         for c in calls:
             c()
@@ -559,15 +564,19 @@ def main():
     if "decode256k" in sections:
         log("section decode256k")
         res["decode256k"] = decode_like_section(ev, synth.long_decode_256k(), K, W, 1, 1,
-                                                "decode_256k_e4m3_bs2048_p64")
+                                                "decode_256k_e4m3_bs2048_p64", fused=True)
     if "decode_b8" in sections:
         log("section decode_b8")
         res["decode_b8"] = decode_like_section(ev, synth.batched_decode_e4m3(), K, W, 8, 1,
                                                "decode_b8_1k4k_e4m3_bs16")
+        res["decode_b8_fused"] = decode_like_section(ev, synth.batched_decode_e4m3(), K, W, 8, 1,
+                                                     "decode_b8_1k4k_e4m3_bs16", fused=True)
     if "decode_b16" in sections:
         log("section decode_b16")
         res["decode_b16"] = decode_like_section(ev, synth.batched_decode_e5m2_16k(), K, W, 2, 1,
                                                 "decode_b16_16k_e5m2_bs16")
+        res["decode_b16_fused"] = decode_like_section(ev, synth.batched_decode_e5m2_16k(), K, W, 2,
+                                                      1, "decode_b16_16k_e5m2_bs16", fused=True)
     if "window" in sections:
         for ctx in (32768, 131072):
             log(f"section window ctx {ctx}")
@@ -660,8 +669,10 @@ def main():
     for key, out_key in [("verify128k", "verify_q8_128k"),
                          ("verify128k_fused", "verify_q8_128k_fused_write"),
                          ("verify_q16", "verify_q16_128k"),
-                         ("decode256k", "decode_256k"), ("decode_b8", "decode_b8"),
-                         ("decode_b16", "decode_b16_16k_e5m2")]:
+                         ("decode256k", "decode_256k_fused_write"), ("decode_b8", "decode_b8"),
+                         ("decode_b8_fused", "decode_b8_fused_write"),
+                         ("decode_b16", "decode_b16_16k_e5m2"),
+                         ("decode_b16_fused", "decode_b16_16k_e5m2_fused_write")]:
         r = res.get(key)
         if r:
             line[out_key] = {"workload": r["name"], "GBps": round(r["GBps"], 1),
