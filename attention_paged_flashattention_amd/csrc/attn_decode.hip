@@ -586,10 +586,17 @@ static void launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream)
                        stream, a);
 }
 
+// The fused write runs in single-block kernels only (the host writes the new
+// tokens with a separate kernel for wider row groups).
 template <int D, int FMT, int QT, int NQB>
 static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
-  if (a.k_new != nullptr) launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream);
-  else launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream);
+  if constexpr (NQB == 1) {
+    if (a.k_new != nullptr) {
+      launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream);
+      return;
+    }
+  }
+  launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream);
 }
 
 template <int D, int FMT, int QT>

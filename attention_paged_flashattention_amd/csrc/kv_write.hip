@@ -186,9 +186,21 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   }
 }
 
+// Slot of new token t when the slots come from the block table: token
+// t % q_len of sequence t / q_len sits at position ctx - q_len + t % q_len
+// (-1, not written, before the sequence start).
+__device__ __forceinline__ int64_t derived_slot(const WriteArgs& a, int t) {
+  const int b = t / a.q_len;
+  const int pos = a.context_lens[b] - a.q_len + (t - b * a.q_len);
+  if (pos < 0) return -1;
+  const int64_t page = a.block_tables[(int64_t)b * a.max_blocks + (pos >> a.bs_log2)];
+  return (page << a.bs_log2) | (pos & ((1 << a.bs_log2) - 1));
+}
+
 // Four dimensions [4q, 4q + 4) of token t, head h: 4 key codes (one store)
-// and 4 value codes (one per dimension row of the value group).
-template <int ST, int FMT>
+// and 4 value codes (one per dimension row of the value group). DERIVED: the
+// slot comes from the block table instead of the slot mapping.
+template <int ST, int FMT, bool DERIVED = false>
 __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int q) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
   // The source values and the scale do not depend on the slot: their loads
@@ -201,7 +213,7 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int
   const float kdiv = ksc ? a.k_scale[h] : 1.0f;
   const float vdiv = vsc ? a.v_scale[h] : 1.0f;
   const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
-  const int64_t slot = a.slots[t];
+  const int64_t slot = DERIVED ? derived_slot(a, t) : a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
   const int off = (int)(slot & ((1 << a.bs_log2) - 1));
@@ -239,6 +251,18 @@ __global__ __launch_bounds__(256) void kv_write_chunks_kernel(const WriteArgs a)
   write_quad<ST, FMT>(a, t, r / nq, r % nq);
 }
 
+// The append form of the same kernel: slots from the block table.
+template <int ST, int FMT>
+__global__ __launch_bounds__(256) void kv_append_kernel(const WriteArgs a) {
+  const int nq = a.head_dim / 4;
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  const int per_token = nq * a.num_kv_heads;
+  if (id >= (int)a.num_tokens * per_token) return;
+  const int t = id / per_token;
+  const int r = id - t * per_token;
+  write_quad<ST, FMT, true>(a, t, r / nq, r % nq);
+}
+
 constexpr int64_t kFewTokens = 64;
 
 template <int ST, int FMT>
@@ -274,6 +298,26 @@ hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStre
     else launch_write<Q_F16, KV_E5M2>(a, stream);
   }
   record_if(ev.stop, stream);
+  return hipGetLastError();
+}
+
+template <int ST, int FMT>
+static void launch_append(const WriteArgs& a, hipStream_t s) {
+  const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
+  hipLaunchKernelGGL((kv_append_kernel<ST, FMT>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, s, a);
+}
+
+hipError_t launch_kv_append(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (fmt == KV_F16) launch_append<Q_F16, KV_F16>(a, stream);
+  else if (fmt == KV_E4M3) {
+    if (src_is_bf16) launch_append<Q_BF16, KV_E4M3>(a, stream);
+    else launch_append<Q_F16, KV_E4M3>(a, stream);
+  } else {
+    if (src_is_bf16) launch_append<Q_BF16, KV_E5M2>(a, stream);
+    else launch_append<Q_F16, KV_E5M2>(a, stream);
+  }
   return hipGetLastError();
 }
 

@@ -18,6 +18,12 @@ struct WriteArgs {
   int num_kv_heads;
   int head_dim;
   int bs_log2;
+  // Slots derived from the block table (kv_append_kernel only): token t is
+  // new token t % q_len of sequence t / q_len, at position ctx - q_len + i.
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int max_blocks;
+  int q_len;
 };
 
 // Split-KV decode / grouped verify.
@@ -79,6 +85,10 @@ ProfileEvents take_profile_events();
 void record_if(hipEvent_t e, hipStream_t stream);
 
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream);
+
+// The newest q_len tokens of each sequence written at their own positions
+// (slots from the block table); records no profiling events.
+hipError_t launch_kv_append(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream);
 
 // fmt: KvFmt, qt: QType, ot: OType. nqb: number of 16-row query blocks.
 hipError_t launch_decode(const DecodeArgs& a, int batch, int head_dim, int fmt, int qt,

@@ -178,6 +178,8 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
                 name, q_len * G, kMaxRows);
   if (num_partitions > kMaxParts)
     return fail(PA_ERR_UNSUPPORTED, "%s: at most %d partitions", name, kMaxParts);
+  if (k_new && (int64_t)batch * q_len * hkv * (head_dim / 4) > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: too many new tokens for one call", name);
   if (batch == 0) return ok();
   const int span = key_span(max_context_len, q_len, window);
   const int req = num_partitions ? num_partitions : auto_partitions(batch, q_len, hkv, span);
@@ -214,14 +216,41 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
   a.num_parts = parts;
   a.window = window < 0 ? -1 : std::min(window, max_context_len);
   a.softmax_scale = softmax_scale;
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
-  a.key_cache_w = k_new ? static_cast<uint8_t*>(const_cast<void*>(kc)) : nullptr;
-  a.value_cache_w = k_new ? static_cast<uint8_t*>(const_cast<void*>(vc)) : nullptr;
   const int nrows = q_len * G;
   const int nqb = nrows <= 16 ? 1 : (nrows <= 32 ? 2 : 4);
-  hipError_t e = pa::launch_decode(a, batch, head_dim, cache_fmt(cache_dtype), q_type(q_dtype),
-                                   out_type(out_dtype), nqb, static_cast<hipStream_t>(stream));
+  hipError_t e = hipSuccess;
+  if (k_new && nqb > 1) {
+    // With more than one 16-row block the fused kernel's main loop compiles
+    // measurably slower than the plain one, so the new tokens are written by a
+    // small kernel first (same encoding, slots from the block table) and the
+    // plain kernel attends.
+    pa::WriteArgs w{};
+    w.key = static_cast<const uint16_t*>(k_new);
+    w.value = static_cast<const uint16_t*>(v_new);
+    w.slots = nullptr;
+    w.num_tokens = (int64_t)batch * q_len;
+    w.key_cache = static_cast<uint8_t*>(const_cast<void*>(kc));
+    w.value_cache = static_cast<uint8_t*>(const_cast<void*>(vc));
+    w.k_scale = a.k_scale;
+    w.v_scale = a.v_scale;
+    w.num_kv_heads = hkv;
+    w.head_dim = head_dim;
+    w.bs_log2 = a.bs_log2;
+    w.block_tables = block_tables;
+    w.context_lens = context_lens;
+    w.max_blocks = max_blocks;
+    w.q_len = q_len;
+    e = pa::launch_kv_append(w, q_dtype == PA_BF16, cache_fmt(cache_dtype),
+                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, name);
+  } else if (k_new) {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.key_cache_w = static_cast<uint8_t*>(const_cast<void*>(kc));
+    a.value_cache_w = static_cast<uint8_t*>(const_cast<void*>(vc));
+  }
+  e = pa::launch_decode(a, batch, head_dim, cache_fmt(cache_dtype), q_type(q_dtype),
+                        out_type(out_dtype), nqb, static_cast<hipStream_t>(stream));
   return hip_status(e, name);
 }
 

@@ -204,9 +204,12 @@ PA_API pa_status attn_verify_paged(
  * tokens of every sequence fused into the decode / verify kernel. The pages
  * write each step's new K/V into the FP8 cache ("1Cat-vLLM 1.0.0" README,
  * "Optional experimental feature: FP8 KV cache") and then attend over it
- * (decode, or the grouped q8 verify of the 1.5.0 notes); here the work-group
- * that will read a new token's keys writes them first, which saves the write
- * kernel's launch and its round trip through HBM of a one-token step.
+ * (decode, or the grouped q8 verify of the 1.5.0 notes). When the rows of one
+ * KV head (q_len * num_q_heads / num_kv_heads) fit one 16-row block, as in
+ * decode, the work-group that will read a new token's keys writes them first,
+ * inside the attention kernel, which saves the write kernel's launch; wider
+ * row groups get a small write kernel (slots from the block table) before the
+ * attention kernel, in the same call.
  *
  * Result (cache bytes and out) identical to
  *     kv_cache_write_fp8(key_new, value_new, q_dtype, slots, batch * q_len, ...)
