@@ -1,5 +1,5 @@
-"""attn_decode_append_paged: the new tokens' quantize-on-write fused into the
-decode / verify kernel.
+"""attn_decode_append_paged: the new tokens' quantize-on-write and the decode /
+verify attention in one call.
 
 Its definition is the two calls it replaces: kv_cache_write_fp8 of the q_len
 newest tokens of every sequence at their own positions, then attn_verify_paged
@@ -8,9 +8,10 @@ cache and requires the fused call's output and both caches to equal the
 two-call result bit for bit, and the output to match the float64 oracle. The
 cases cover every cache format and query dtype, pages below and above one
 64-key tile, head_dim 64 and 128, q_len 1 to 16, sequences shorter than q_len
-(their missing positions are not written), an empty context, and new tokens
-that straddle a partition boundary (two work-groups write one sequence's
-tokens).
+(their missing positions are not written), an empty context, new tokens that
+straddle a partition boundary (two work-groups write one sequence's tokens),
+and both forms of the call: the write inside the attention kernel (at most 16
+rows per KV head) and the write kernel with block-table slots ahead of it.
 """
 
 import numpy as np
@@ -75,6 +76,11 @@ CASES = [
     ("e4m3", "bf16", 3, (130, 63), 32, 64, 8, 2, 0),
     ("f16", "f16", 4, (100, 33), 32, 64, 8, 2, 0),
     ("f16", "f16", 1, (257, 1), 16, 128, 16, 2, 0),
+    # more than 16 rows per KV head: the write kernel with block-table slots
+    # runs before the plain kernel
+    ("f16", "f16", 8, (100, 33), 32, 64, 8, 2, 0),
+    ("e4m3", "bf16", 5, (300, 4), 16, 128, 32, 8, 0),
+    ("e5m2", "f16", 16, (70, 1000, 16), 16, 64, 16, 4, 3),
 ]
 
 
