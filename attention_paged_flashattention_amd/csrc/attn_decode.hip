@@ -576,59 +576,61 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
 }
 
 template <int D, int FMT, int QT, int NQB, bool APPEND>
-static void launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream) {
+static void launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream,
+                             const ProfileEvents& ev) {
   dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
   if (a.bs_log2 >= 6)
-    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, true, APPEND>), grid, dim3(256), 0,
-                       stream, a);
+    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, true, APPEND>, grid, dim3(256), 0, stream,
+                  ev, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, FMT, QT, NQB, false, APPEND>), grid, dim3(256), 0,
-                       stream, a);
+    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, false, APPEND>, grid, dim3(256), 0, stream,
+                  ev, a);
 }
 
 // The fused write runs in single-block kernels only (the host writes the new
 // tokens with a separate kernel for wider row groups).
 template <int D, int FMT, int QT, int NQB>
-static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream) {
+static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream,
+                         const ProfileEvents& ev) {
   if constexpr (NQB == 1) {
     if (a.k_new != nullptr) {
-      launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream);
+      launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream, ev);
       return;
     }
   }
-  launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream);
+  launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream, ev);
 }
 
 template <int D, int FMT, int QT>
-static void launch_split_nqb(const DecodeArgs& a, int batch, int nqb, hipStream_t stream) {
-  if (nqb == 1) launch_split<D, FMT, QT, 1>(a, batch, stream);
-  else if (nqb == 2) launch_split<D, FMT, QT, 2>(a, batch, stream);
-  else launch_split<D, FMT, QT, 4>(a, batch, stream);
+static void launch_split_nqb(const DecodeArgs& a, int batch, int nqb, hipStream_t stream,
+                             const ProfileEvents& ev) {
+  if (nqb == 1) launch_split<D, FMT, QT, 1>(a, batch, stream, ev);
+  else if (nqb == 2) launch_split<D, FMT, QT, 2>(a, batch, stream, ev);
+  else launch_split<D, FMT, QT, 4>(a, batch, stream, ev);
 }
 
 template <int D, int FMT>
 static void launch_combine(const DecodeArgs& a, int64_t rows, int ot, hipStream_t stream) {
   dim3 grid((unsigned)rows), block(kCombineThreads);
-  if (ot == O_F32) hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_F32>), grid, block, 0, stream, a);
-  else if (ot == O_F16) hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_F16>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((decode_combine_kernel<D, FMT, O_BF16>), grid, block, 0, stream, a);
+  const ProfileEvents none{};
+  if (ot == O_F32) launch_kernel(decode_combine_kernel<D, FMT, O_F32>, grid, block, 0, stream, none, a);
+  else if (ot == O_F16) launch_kernel(decode_combine_kernel<D, FMT, O_F16>, grid, block, 0, stream, none, a);
+  else launch_kernel(decode_combine_kernel<D, FMT, O_BF16>, grid, block, 0, stream, none, a);
 }
 
 template <int D>
 static void launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int ot, int nqb,
                             hipStream_t stream) {
   const ProfileEvents ev = take_profile_events();
-  record_if(ev.start, stream);
   if (fmt == KV_F16) {
-    launch_split_nqb<D, KV_F16, Q_F16>(a, batch, nqb, stream);
+    launch_split_nqb<D, KV_F16, Q_F16>(a, batch, nqb, stream, ev);
   } else if (fmt == KV_E4M3) {
-    if (qt == Q_BF16) launch_split_nqb<D, KV_E4M3, Q_BF16>(a, batch, nqb, stream);
-    else launch_split_nqb<D, KV_E4M3, Q_F16>(a, batch, nqb, stream);
+    if (qt == Q_BF16) launch_split_nqb<D, KV_E4M3, Q_BF16>(a, batch, nqb, stream, ev);
+    else launch_split_nqb<D, KV_E4M3, Q_F16>(a, batch, nqb, stream, ev);
   } else {
-    if (qt == Q_BF16) launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream);
-    else launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream);
+    if (qt == Q_BF16) launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream, ev);
+    else launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream, ev);
   }
-  record_if(ev.stop, stream);
   const int64_t rows = (int64_t)batch * a.q_len * a.num_q_heads;
   if (fmt == KV_F16) launch_combine<D, KV_F16>(a, rows, ot, stream);
   else if (fmt == KV_E4M3) launch_combine<D, KV_E4M3>(a, rows, ot, stream);

@@ -431,23 +431,24 @@ void prefill_kernel(const PrefillArgs a) {
 }
 
 template <int D, int FMT, int QT>
-static void launch_pf(const PrefillArgs& a, int ot, hipStream_t s) {
+static void launch_pf(const PrefillArgs& a, int ot, hipStream_t s, const ProfileEvents& ev) {
   const unsigned nblk = (unsigned)((int64_t)a.num_kv_heads * a.q_blocks * a.batch);
   dim3 grid(nblk), block(kPrefillThreads);
-  if (ot == O_F32) hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_F32>), grid, block, 0, s, a);
-  else if (ot == O_F16) hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_F16>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((prefill_kernel<D, FMT, QT, O_BF16>), grid, block, 0, s, a);
+  if (ot == O_F32) launch_kernel(prefill_kernel<D, FMT, QT, O_F32>, grid, block, 0, s, ev, a);
+  else if (ot == O_F16) launch_kernel(prefill_kernel<D, FMT, QT, O_F16>, grid, block, 0, s, ev, a);
+  else launch_kernel(prefill_kernel<D, FMT, QT, O_BF16>, grid, block, 0, s, ev, a);
 }
 
 template <int D>
-static void launch_pf_d(const PrefillArgs& a, int fmt, int qt, int ot, hipStream_t s) {
-  if (fmt == KV_F16) launch_pf<D, KV_F16, Q_F16>(a, ot, s);
+static void launch_pf_d(const PrefillArgs& a, int fmt, int qt, int ot, hipStream_t s,
+                        const ProfileEvents& ev) {
+  if (fmt == KV_F16) launch_pf<D, KV_F16, Q_F16>(a, ot, s, ev);
   else if (fmt == KV_E4M3) {
-    if (qt == Q_BF16) launch_pf<D, KV_E4M3, Q_BF16>(a, ot, s);
-    else launch_pf<D, KV_E4M3, Q_F16>(a, ot, s);
+    if (qt == Q_BF16) launch_pf<D, KV_E4M3, Q_BF16>(a, ot, s, ev);
+    else launch_pf<D, KV_E4M3, Q_F16>(a, ot, s, ev);
   } else {
-    if (qt == Q_BF16) launch_pf<D, KV_E5M2, Q_BF16>(a, ot, s);
-    else launch_pf<D, KV_E5M2, Q_F16>(a, ot, s);
+    if (qt == Q_BF16) launch_pf<D, KV_E5M2, Q_BF16>(a, ot, s, ev);
+    else launch_pf<D, KV_E5M2, Q_F16>(a, ot, s, ev);
   }
 }
 
@@ -455,10 +456,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int fmt, int qt, i
                           hipStream_t stream) {
   if (a.batch == 0 || a.q_blocks == 0) return hipSuccess;
   const ProfileEvents ev = take_profile_events();
-  record_if(ev.start, stream);
-  if (head_dim == 64) launch_pf_d<64>(a, fmt, qt, ot, stream);
-  else launch_pf_d<128>(a, fmt, qt, ot, stream);
-  record_if(ev.stop, stream);
+  if (head_dim == 64) launch_pf_d<64>(a, fmt, qt, ot, stream, ev);
+  else launch_pf_d<128>(a, fmt, qt, ot, stream, ev);
   return hipGetLastError();
 }
 

@@ -266,46 +266,44 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const WriteArgs a) {
 constexpr int64_t kFewTokens = 64;
 
 template <int ST, int FMT>
-static void launch_write(const WriteArgs& a, hipStream_t s) {
+static void launch_write(const WriteArgs& a, hipStream_t s, const ProfileEvents& ev) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
   const size_t rows_lds = (size_t)a.head_dim * kRowTokens * ES;
   if (a.num_tokens < kFewTokens) {
     const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
-    hipLaunchKernelGGL((kv_write_chunks_kernel<ST, FMT>), dim3((unsigned)((total + 255) / 256)),
-                       dim3(256), 0, s, a);
+    launch_kernel(kv_write_chunks_kernel<ST, FMT>, dim3((unsigned)((total + 255) / 256)),
+                  dim3(256), 0, s, ev, a);
   } else if (a.head_dim == 64 || a.head_dim == 128) {
     dim3 grid((unsigned)((a.num_tokens + kRowTokens - 1) / kRowTokens), (unsigned)a.num_kv_heads);
     if (a.head_dim == 64)
-      hipLaunchKernelGGL((kv_write_rows_kernel<ST, FMT, 64>), grid, dim3(256), rows_lds, s, a);
+      launch_kernel(kv_write_rows_kernel<ST, FMT, 64>, grid, dim3(256), (uint32_t)rows_lds, s, ev, a);
     else
-      hipLaunchKernelGGL((kv_write_rows_kernel<ST, FMT, 128>), grid, dim3(256), rows_lds, s, a);
+      launch_kernel(kv_write_rows_kernel<ST, FMT, 128>, grid, dim3(256), (uint32_t)rows_lds, s, ev, a);
   } else {
     dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads);
-    hipLaunchKernelGGL((kv_write_tokens_kernel<ST, FMT>), grid, dim3(256), 0, s, a);
+    launch_kernel(kv_write_tokens_kernel<ST, FMT>, grid, dim3(256), 0, s, ev, a);
   }
 }
 
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   const ProfileEvents ev = take_profile_events();
-  record_if(ev.start, stream);
-  if (fmt == KV_F16) launch_write<Q_F16, KV_F16>(a, stream);
+  if (fmt == KV_F16) launch_write<Q_F16, KV_F16>(a, stream, ev);
   else if (fmt == KV_E4M3) {
-    if (src_is_bf16) launch_write<Q_BF16, KV_E4M3>(a, stream);
-    else launch_write<Q_F16, KV_E4M3>(a, stream);
+    if (src_is_bf16) launch_write<Q_BF16, KV_E4M3>(a, stream, ev);
+    else launch_write<Q_F16, KV_E4M3>(a, stream, ev);
   } else {
-    if (src_is_bf16) launch_write<Q_BF16, KV_E5M2>(a, stream);
-    else launch_write<Q_F16, KV_E5M2>(a, stream);
+    if (src_is_bf16) launch_write<Q_BF16, KV_E5M2>(a, stream, ev);
+    else launch_write<Q_F16, KV_E5M2>(a, stream, ev);
   }
-  record_if(ev.stop, stream);
   return hipGetLastError();
 }
 
 template <int ST, int FMT>
 static void launch_append(const WriteArgs& a, hipStream_t s) {
   const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
-  hipLaunchKernelGGL((kv_append_kernel<ST, FMT>), dim3((unsigned)((total + 255) / 256)), dim3(256),
-                     0, s, a);
+  launch_kernel(kv_append_kernel<ST, FMT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                ProfileEvents{}, a);
 }
 
 hipError_t launch_kv_append(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream) {

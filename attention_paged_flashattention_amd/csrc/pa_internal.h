@@ -1,6 +1,7 @@
 // Host-side internal interface between the C ABI layer and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,7 +83,20 @@ struct ProfileEvents {
   hipEvent_t stop = nullptr;
 };
 ProfileEvents take_profile_events();
-void record_if(hipEvent_t e, hipStream_t stream);
+
+// Launches kernel(a) on stream s. With profiling events pending they are
+// attached to this kernel's own dispatch (hipExtLaunchKernel), so the pair
+// times the kernel alone, without the latency of separate marker packets.
+template <typename Arg>
+inline void launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, uint32_t shmem,
+                          hipStream_t s, const ProfileEvents& ev, const Arg& a) {
+  void* args[] = {const_cast<Arg*>(&a)};
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  if (ev.start && ev.stop)
+    (void)hipExtLaunchKernel(fn, grid, block, args, shmem, s, ev.start, ev.stop, 0);
+  else
+    (void)hipLaunchKernel(fn, grid, block, args, shmem, s);
+}
 
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream);
 

@@ -262,9 +262,6 @@ ProfileEvents take_profile_events() {
   g_profile = ProfileEvents{};
   return e;
 }
-void record_if(hipEvent_t e, hipStream_t stream) {
-  if (e) (void)hipEventRecord(e, stream);
-}
 }  // namespace pa
 
 extern "C" {

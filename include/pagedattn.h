@@ -305,10 +305,11 @@ PA_API const char* pa_version(void);
  * Profiling hook (in the spirit of the pages' per-route performance counters,
  * "SM70 release profile and acceleration status"): start_event and stop_event
  * are hipEvent_t handles owned by the caller. The next write or attention call
- * made on the calling thread records start_event on its stream immediately
- * before its main kernel (the write kernel, the prefill kernel, or the split
- * kernel of decode/verify) and stop_event immediately after it, then forgets
- * both. Passing NULL for either clears a pending request. No effect on results.
+ * made on the calling thread attaches both to the dispatch of its main kernel
+ * (the write kernel, the prefill kernel, or the split kernel of decode /
+ * verify; hipExtLaunchKernel), so they record that kernel's start and end,
+ * then forgets both. Passing NULL for either clears a pending request. No
+ * effect on results.
  */
 PA_API void pa_profile_next_call(void* start_event, void* stop_event);
 
