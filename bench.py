@@ -201,8 +201,8 @@ def decode_like_section(ev, case, steps, warmup, copies, q_len, name, window=Non
 
     # the step rate from a loop with no events; the split kernel's launch
     # durations from a second timed loop of the same steps with an event pair
-    # around every split launch (each recorded event costs the stream a few
-    # microseconds, which would otherwise be billed to the step)
+    # attached to every split launch (events still cost the stream a little,
+    # which would otherwise be billed to the step)
     ms = timed(lambda i, rec: step(i, False), steps, warmup)
     ms_ev = timed(step, steps, 0)
     kern = [ev.elapsed_ms(a, b) for a, b in zip(starts, stops)]
