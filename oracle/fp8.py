@@ -87,7 +87,10 @@ def to_float32_scaled(x, scale=None):
     correct rounding); y = float32(x) when no scale is given."""
     y = np.asarray(x).astype(np.float32)
     if scale is not None:
-        y = y / np.float32(scale)
+        # a quotient beyond the float32 range is +-inf, as IEEE division gives
+        # it; round_to_grid saturates it (numpy's overflow warning is muted)
+        with np.errstate(over="ignore"):
+            y = y / np.float32(scale)
     return y
 
 
