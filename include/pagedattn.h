@@ -13,8 +13,9 @@
  *   attn_verify_paged   -- the grouped speculative-verify step: q_len new
  *                          causal tokens per sequence (q_len = 8 is the q8
  *                          verifier: seven drafts plus one);
- *   attn_decode_append_paged -- decode / verify with the new tokens'
- *                          quantize-on-write fused into the same kernel.
+ *   attn_decode_append_paged -- decode / verify and the new tokens'
+ *                          quantize-on-write in one call (inside the attention
+ *                          kernel when one 16-row block holds a KV head's rows).
  *
  * Semantics shared by the attention calls. Sequence b has context_lens[b]
  * keys, counting its new tokens (which must already be in the cache: write,
