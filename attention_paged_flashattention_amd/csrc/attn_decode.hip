@@ -166,9 +166,10 @@ struct DecodePipe {
   static constexpr bool value = FMT != KV_F16 && NQB == 1;
 };
 
-// APPEND: the fused quantize-on-write of the new tokens (a separate
-// instantiation, so the plain decode / verify kernels carry none of its code).
-template <int D, int FMT, int QT, int NQB, bool UNI, bool APPEND>
+// APPEND: the fused quantize-on-write of the new tokens. ONEP: a single
+// partition, whose work-group stores the normalised output itself. Both are
+// separate instantiations, so the other kernels carry none of their code.
+template <int D, int FMT, int QT, int NQB, bool UNI, bool APPEND, bool ONEP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodePipe<FMT, NQB>::value ? 2 : 1)))
 void decode_split_kernel(const DecodeArgs a) {
   constexpr bool PIPE = DecodePipe<FMT, NQB>::value;
@@ -438,8 +439,12 @@ void decode_split_kernel(const DecodeArgs a) {
   }
 
   // Merge the 4 waves' states for each 16-row block and write one partial per
-  // row: (max, sum) and the unnormalised output, all relative to the max.
+  // row: (max, sum) and the unnormalised output, all relative to the max. With
+  // a single partition the merged state is the whole row: it is normalised and
+  // stored here (the combine's arithmetic for one partition), and no combine
+  // kernel runs.
   const int64_t P = a.num_parts;
+  [[maybe_unused]] const float vscale = ONEP ? (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>() : 0.0f;
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     float lf = l[nb];
@@ -471,6 +476,14 @@ void decode_split_kernel(const DecodeArgs a) {
       }
       const int qi = r / G, h = g * G + r % G;
       const int64_t rowg = (int64_t)(b * a.q_len + qi) * a.num_q_heads + h;
+      if constexpr (ONEP) {
+        const float f = lt > 0.0f ? vscale / lt : 0.0f;
+        const int64_t idx = rowg * D + d;
+        if (a.out_type == O_F32) store_out<O_F32>(a.out, idx, acc * f);
+        else if (a.out_type == O_F16) store_out<O_F16>(a.out, idx, acc * f);
+        else store_out<O_BF16>(a.out, idx, acc * f);
+        continue;
+      }
       a.ws_o[(rowg * P + p) * D + d] = acc;
       if (d == 0) {
         a.ws_ml[(rowg * P + p) * 2] = M;
@@ -575,16 +588,30 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
   }
 }
 
+template <int D, int FMT, int QT, int NQB, bool APPEND, bool ONEP>
+static void launch_split_k(const DecodeArgs& a, int batch, hipStream_t stream,
+                           const ProfileEvents& ev) {
+  dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
+  if (a.bs_log2 >= 6)
+    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, true, APPEND, ONEP>, grid, dim3(256), 0,
+                  stream, ev, a);
+  else
+    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, false, APPEND, ONEP>, grid, dim3(256), 0,
+                  stream, ev, a);
+}
+
+// One partition (decode and q8-wide verify): the split kernel writes the
+// output and the combine is not launched.
 template <int D, int FMT, int QT, int NQB, bool APPEND>
 static void launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream,
                              const ProfileEvents& ev) {
-  dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
-  if (a.bs_log2 >= 6)
-    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, true, APPEND>, grid, dim3(256), 0, stream,
-                  ev, a);
-  else
-    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, false, APPEND>, grid, dim3(256), 0, stream,
-                  ev, a);
+  if constexpr (NQB <= 2) {
+    if (a.num_parts == 1) {
+      launch_split_k<D, FMT, QT, NQB, APPEND, true>(a, batch, stream, ev);
+      return;
+    }
+  }
+  launch_split_k<D, FMT, QT, NQB, APPEND, false>(a, batch, stream, ev);
 }
 
 // The fused write runs in single-block kernels only (the host writes the new
@@ -631,6 +658,7 @@ static void launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int
     if (qt == Q_BF16) launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream, ev);
     else launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream, ev);
   }
+  if (a.num_parts == 1 && nqb <= 2) return;   // the split kernel stored the output
   const int64_t rows = (int64_t)batch * a.q_len * a.num_q_heads;
   if (fmt == KV_F16) launch_combine<D, KV_F16>(a, rows, ot, stream);
   else if (fmt == KV_E4M3) launch_combine<D, KV_E4M3>(a, rows, ot, stream);

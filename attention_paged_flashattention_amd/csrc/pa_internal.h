@@ -55,6 +55,7 @@ struct DecodeArgs {
   const uint16_t* v_new;
   uint8_t* key_cache_w;     // the caches above, for the fused write
   uint8_t* value_cache_w;
+  int out_type;             // OType of out (stored by the split kernel when num_parts == 1)
 };
 
 struct PrefillArgs {

@@ -215,6 +215,7 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
   a.part_len = part_len;
   a.num_parts = parts;
   a.window = window < 0 ? -1 : std::min(window, max_context_len);
+  a.out_type = out_type(out_dtype);
   a.softmax_scale = softmax_scale;
   const int nrows = q_len * G;
   const int nqb = nrows <= 16 ? 1 : (nrows <= 32 ? 2 : 4);

@@ -144,6 +144,8 @@ DECODE_CASES = [
     ("f16", 2, (65, 300), 4, 1, 64, 16, "f16", 0),
     ("f16", 1, (1000,), 8, 8, 64, 16, "f16", 4),
     ("e4m3", 2, (100, 513), 8, 2, 64, 16, "f16", 2),
+    # one partition: the split kernel stores the output (no combine), bf16 out
+    ("e4m3", 2, (129, 300), 32, 8, 128, 32, "bf16", 1),
 ]
 
 
@@ -170,6 +172,8 @@ VERIFY_CASES = [
     ("e4m3", 2, (40, 600), 3, 32, 8, 128, 16, 0),
     ("f16", 2, (64, 300), 8, 4, 1, 64, 16, 0),
     ("e5m2", 1, (129,), 1, 32, 8, 128, 16, 0),
+    ("e5m2", 2, (8, 200), 8, 32, 8, 128, 64, 1),      # 32 rows, one partition
+    ("e4m3", 2, (16, 900), 16, 32, 8, 128, 2048, 1),  # 64 rows, one partition (combine kept)
 ]
 
 
