@@ -28,7 +28,11 @@
 //   lane-partial until the end.
 // * The 4 waves' (m, l, O) are merged through LDS, and each work-group writes
 //   one partial per row; the combine kernel merges the partitions in a fixed
-//   order, so results are bitwise reproducible.
+//   order, so results are bitwise reproducible. With a single partition the
+//   work-group stores the normalised row itself and no combine runs.
+// * The new tokens of a decode step can be written by the same kernel
+//   (quantize-on-write fused in): the work-group whose keys hold them writes
+//   them before its first load.
 // * The same kernels run the draft model's non-causal sliding-window attention
 //   ("1Cat-vLLM 1.5.0", "Production DFlash2 on V100"; "Flash-V100 long-context
 //   improvements": prefix tiles outside the window are skipped): rows see keys
