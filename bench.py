@@ -32,6 +32,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -87,10 +88,15 @@ class HipEvents:
 
 
 def source_hash(*names):
+    """Hash of the named kernel sources with comments and whitespace removed:
+    counters stay attached to the code they were taken on, not its comments."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "attention_paged_flashattention_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "attention_paged_flashattention_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
