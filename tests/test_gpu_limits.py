@@ -70,3 +70,29 @@ def test_widest_row_group(runner, fmt, q_len):
     out = dc.verify(q_len, out_dtype=torch.float32)
     torch.cuda.synchronize()
     check_close(out.reshape(-1, hq, 128), oracle_full(case), fmt, "64-row group")
+
+
+def test_prefill_largest_page_size(runner):
+    """A 1000-token prefill chunk straddling the boundary of two 65536-token
+    pages (positions 65000..65999), bf16 Q and E4M3 cache: sampled rows of
+    every query head against the oracle."""
+    case = synth.make_case("bs65536-prefill", 44, [66000], [66000], 8, 2, 128, 65536, "bf16",
+                           "bf16", "e4m3")
+    log(case.name)
+    dc = runner.DeviceCase(case)
+    dc.write_tokens(0, 65000)
+    out = dc.prefill_chunk(65000, 66000, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kc, vc = oracle_cache_heads(case, [(0, 0), (0, 1)])
+    q32 = synth.to_f32(case.q, "bf16")
+    rng = np.random.default_rng(5)
+    pos = np.unique(np.concatenate([[65000, 65535, 65536, 65999], rng.integers(65000, 66000, 8)]))
+    rows_q, rows_h, rows_p = [], [], []
+    for p in pos:
+        for h in range(8):
+            rows_q.append(q32[p, h])
+            rows_h.append(h)
+            rows_p.append(int(p))
+    ref = oracle_rows(case, kc, vc, 0, np.array(rows_q), rows_h, rows_p)
+    got = out.cpu()[torch.tensor(np.array(rows_p) - 65000), torch.tensor(rows_h)]
+    check_close(got, ref, "e4m3", "prefill across 65536-token pages")
