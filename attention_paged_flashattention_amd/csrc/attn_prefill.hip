@@ -7,9 +7,9 @@
 // several query heads onto one KV head's tensor-core work, measured in
 // useful causal FLOP/s). How it is done here (gfx950):
 //
-// * Work-group = 256 rows that share one KV head: 256/G query tokens x the G
-//   query heads of that KV head (GQA packing), 8 waves x 32 rows, two waves
-//   per SIMD.
+// * Work-group = 256 rows that share one KV head: floor(256/G) query tokens x
+//   the G query heads of that KV head (GQA packing; any G up to 64, the rows
+//   past the last whole token idle), 8 waves x 32 rows, two waves per SIMD.
 // * The grid is ordered so that consecutive work-groups take consecutive KV
 //   heads: with round-robin dispatch over the 8 XCDs, each XCD's L2 holds the
 //   K/V of one head while all its work-groups stream it. Query tiles with the

@@ -84,6 +84,9 @@ int out_type(pa_dtype d) {
 constexpr int kMinBlock = 16;
 constexpr int kMaxBlock = 1 << 16;
 constexpr int kMaxRows = 64;       // q_len * G of one decode/verify group
+// Query heads per KV head in prefill: a work-group's 256 rows hold
+// floor(256 / G) whole tokens (the last 256 mod G rows idle), at least 4.
+constexpr int kMaxPrefillGroup = 64;
 constexpr int kTile = 64;          // keys per decode tile
 constexpr int kMaxParts = 4096;
 
@@ -346,9 +349,10 @@ PA_API pa_status attn_prefill_paged(const void* q, pa_dtype q_dtype, const int32
   if (max_q_len > max_context_len)
     return fail(PA_ERR_INVALID_ARG, "attn_prefill_paged: max_q_len exceeds max_context_len");
   const int G = num_q_heads / num_kv_heads;
-  if (G > 32 || !is_pow2(G))
+  if (G > kMaxPrefillGroup)
     return fail(PA_ERR_UNSUPPORTED,
-                "attn_prefill_paged: num_q_heads / num_kv_heads = %d unsupported (power of two <= 32)", G);
+                "attn_prefill_paged: num_q_heads / num_kv_heads = %d unsupported (at most %d)", G,
+                kMaxPrefillGroup);
   if (batch == 0 || max_q_len == 0 || total_q == 0) return ok();
   pa::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -501,7 +505,7 @@ PA_API int pa_supports(int op, pa_dtype q_dtype, pa_dtype cache_dtype, int head_
   if (q_type(q_dtype) < 0 || cache_fmt(cache_dtype) < 0) return 0;
   if (cache_dtype == PA_F16 && q_dtype != PA_F16) return 0;
   if (head_dim != 64 && head_dim != 128) return 0;
-  if (op == PA_OP_PREFILL) return q_len >= 0 && G <= 32 && is_pow2(G);
+  if (op == PA_OP_PREFILL) return q_len >= 0 && G <= kMaxPrefillGroup;
   if (op == PA_OP_DECODE) return q_len == 1 && G <= kMaxRows;
   if (op == PA_OP_VERIFY || op == PA_OP_WINDOW) return q_len >= 1 && (int64_t)q_len * G <= kMaxRows;
   return 0;

@@ -139,6 +139,8 @@ PA_API pa_status kv_cache_write_fp8(
  *   context_lens [batch] int32, keys of sequence b including its new chunk
  *   k_scale, v_scale [num_kv_heads] float32 (see kv_cache_write_fp8)
  *   out          [total_q][num_q_heads][head_dim], out_dtype F32, F16 or BF16
+ * num_q_heads / num_kv_heads may be any value up to 64 (PA_ERR_UNSUPPORTED
+ * above).
  */
 PA_API pa_status attn_prefill_paged(
     const void* q, pa_dtype q_dtype, const int32_t* cu_seqlens_q, int batch,

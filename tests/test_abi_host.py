@@ -165,8 +165,7 @@ def test_prefill_rejects_before_launch(pa):
                                     a["vs"], a["scale"], a["out"], a["odt"], a["stream"])
     assert call(cu=NUL) == 1
     assert call(maxq=5000) == 1
-    assert call(hq=24, hkv=8) == 2           # G = 3 is not a power of two
-    assert call(hq=64, hkv=1) == 2           # G = 64 > 32
+    assert call(hq=65, hkv=1) == 2           # G = 65 > 64
     assert call(B=-1) == 1
     assert call(B=0) == 0
     assert call(totq=0) == 0
@@ -183,6 +182,9 @@ def test_supports_table(pa):
     assert s(pa.PA_OP_PREFILL, BF16, E4, 128, 32, 8, 2048, 4096)
     assert s(pa.PA_OP_PREFILL, F16, F16, 64, 4, 1, 16, 64)
     assert not s(pa.PA_OP_PREFILL, BF16, F16, 64, 4, 1, 16, 64)
+    assert s(pa.PA_OP_PREFILL, BF16, E4, 128, 48, 8, 2048, 4096)     # G = 6
+    assert s(pa.PA_OP_PREFILL, F16, E5, 128, 64, 1, 16, 64)          # G = 64
+    assert not s(pa.PA_OP_PREFILL, F16, E5, 128, 65, 1, 16, 64)
     assert not s(pa.PA_OP_DECODE, F16, E4, 96, 32, 8, 16, 1)
     assert not s(pa.PA_OP_DECODE, F16, E4, 128, 32, 8, 24, 1)
     assert s(pa.PA_OP_WRITE, BF16, E4, 128, 8, 8, 2048, 0)

@@ -260,6 +260,11 @@ PREFILL_CASES = [
     ("e5m2", 200, 200, 8, 8, 64, 16, "bf16"),
     ("f16", 300, 128, 8, 4, 128, 16, "f16"),
     ("e4m3", 130, 65, 32, 1, 64, 16, "f16"),
+    # GQA ratios that are not powers of two (six query heads per KV head, the
+    # packing the pages' long-prefill kernel uses; three) and the largest (64)
+    ("e4m3", 600, 300, 48, 8, 128, 2048, "bf16"),
+    ("e5m2", 257, 129, 12, 4, 64, 16, "f16"),
+    ("e4m3", 100, 50, 64, 1, 128, 64, "bf16"),
 ]
 
 
