@@ -407,3 +407,36 @@ def test_window_covering_the_context_equals_last_position_decode(runner):
     for i in range(8):
         od = dc.decode(q=qv[:, i].contiguous(), out_dtype=torch.float32)
         assert torch.max(torch.abs(od - out[:, i])).item() < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# the synchronous table check
+# ---------------------------------------------------------------------------
+
+def test_validate_tables(runner):
+    """pa_validate_tables accepts a workload's own tables (block-table padding
+    past the used pages is not looked at) and names the first bad entry."""
+    from attention_paged_flashattention_amd import pagedattn as pa
+    case = _mk("e4m3", 3, (100, 17, 0), 1)
+    dc = runner.DeviceCase(case)
+    bs, nb = case.block_size, case.num_blocks
+    pa.pa_validate_tables(dc.block_tables, dc.ctx_lens, dc.max_ctx, bs, nb)
+
+    def rejects(bt, cl, max_ctx=dc.max_ctx, what=""):
+        with pytest.raises(pa.PagedAttnError) as e:
+            pa.pa_validate_tables(bt, cl, max_ctx, bs, nb)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
+        assert what in str(e.value), str(e.value)
+
+    bt = dc.block_tables.clone()
+    bt[1, 1] = nb                              # a used page id out of range
+    rejects(bt, dc.ctx_lens, what="block_tables[1][1]")
+    bt = dc.block_tables.clone()
+    bt[0, 6] = -1                              # last used page of a 100-key sequence
+    rejects(bt, dc.ctx_lens, what="block_tables[0][6]")
+    cl = dc.ctx_lens.clone()
+    cl[2] = dc.max_ctx + 1                     # longer than max_context_len
+    rejects(dc.block_tables, cl, what="context_lens[2]")
+    cl = dc.ctx_lens.clone()
+    cl[1] = -3
+    rejects(dc.block_tables, cl, what="context_lens[1]")
