@@ -371,8 +371,8 @@ def bind_attn_window_paged(q, window_left, key_cache, value_cache, cache_dtype, 
 
 
 def pa_profile_next_call(start_event, stop_event):
-    """Record the two hipEvent_t handles (ints) around the main kernel of the
-    next call on this thread."""
+    """Attach the two hipEvent_t handles (ints) to the main kernel of the next
+    call on this thread (they record its start and end); None clears."""
     _lib.pa_profile_next_call(ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event))
 
 

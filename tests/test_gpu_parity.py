@@ -440,3 +440,41 @@ def test_validate_tables(runner):
     cl = dc.ctx_lens.clone()
     cl[1] = -3
     rejects(dc.block_tables, cl, what="context_lens[1]")
+
+
+def test_profiling_hook(runner):
+    """pa_profile_next_call: the next call's main kernel carries the event pair
+    (positive duration) and computes the same result as an unprofiled call."""
+    import ctypes
+    from attention_paged_flashattention_amd import pagedattn as pa
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+
+    def event():
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed(a, b):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    case = _mk("e4m3", 2, (700, 3000), 1, bs=64)
+    dc = runner.DeviceCase(case)
+    a, b = event(), event()
+    pa.pa_profile_next_call(a, b)
+    dc.write_all()                                 # the write kernel carries the events
+    torch.cuda.synchronize()
+    assert elapsed(a, b) > 0.0
+    ref = dc.decode(out_dtype=torch.float32)
+    a, b = event(), event()
+    pa.pa_profile_next_call(a, b)
+    out = dc.decode(out_dtype=torch.float32)       # the split kernel carries them
+    torch.cuda.synchronize()
+    assert elapsed(a, b) > 0.0
+    assert torch.equal(out, ref)
+    pa.pa_profile_next_call(event(), event())
+    pa.pa_profile_next_call(None, None)            # a pending request can be cleared
+    assert torch.equal(dc.decode(out_dtype=torch.float32), ref)
