@@ -7,20 +7,24 @@ Prints ONE JSON line. ``value`` is the headline: decode at 128K context over
 an FP8 E4M3 block-paged cache (1 sequence, 32 query / 8 KV heads, head_dim 128,
 2048-token pages, 64 split-KV partitions), in GB/s of algorithmic bytes. One
 step = quantize-on-write of the newest token, the split-KV kernel and the
-log-sum-exp combine -- every step of the decode path. Four copies of the 256 MiB
+log-sum-exp combine -- every step of the decode path -- issued as one
+attn_decode_append_paged call (the write runs inside the split kernel); the
+same step as two calls (write kernel, then attn_decode_paged) and replayed from
+a HIP graph are reported beside it. Four copies of the 256 MiB
 cache are used in rotation so that no step finds its cache in the 256 MB
 last-level cache. The same line carries the 32K chunked-prefill throughput
 (useful causal TFLOP/s; one step = 8 chunks of 4096 tokens, each a write then a
 prefill), the q8 and q16 verify at 128K, the 256K decode, the batched decodes
 (8 x 1K-4K E4M3, 16 x 16K E5M2), the draft's sliding-window attention at 32K
-and 128K, the 64K prefill in 4096- and 8192-token chunks, the write kernel's rate, the small prefill+decode workload's latency,
+and 128K, the 64K prefill in 4096- and 8192-token chunks, the write kernel's
+rate, the small prefill+decode workload's latency,
 the cost of a decode call with nothing to read, the roofline of the dominant
 kernels, and the CPU oracle timed on a bounded sample of the headline
 workload.
 
 Each section times its steps twice: a plain loop gives the step rate, and a
-second loop of the same steps, with timing-only HIP events recorded by the
-library around every launch of the dominant kernel on its stream, gives that
+second loop of the same steps, with timing-only HIP events that the library
+attaches to every launch of the dominant kernel on its stream, gives that
 kernel's launch durations (average, and 10th/50th/90th percentiles).
 
 Inputs are synthetic and seeded (attention_paged_flashattention_amd.synth) and
