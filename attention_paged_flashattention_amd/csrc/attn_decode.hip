@@ -101,7 +101,7 @@ struct DecodeTile {
 // Physical pages of the two 16-key runs a lane touches in a tile (its K run
 // and its V run). With pages of >= 64 keys both are the tile's one page.
 struct TilePages {
-  int64_t k, v;
+  int32_t k, v;
 };
 
 __device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
@@ -119,8 +119,8 @@ __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, int b, in
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
   constexpr int CH = D / 8;                   // 16-byte source chunks per row
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
-  const float kdiv = ksc ? a.k_scale[g] : 1.0f;
-  const float vdiv = vsc ? a.v_scale[g] : 1.0f;
+  const float kdiv = ksc ? ld_const(a.k_scale, g) : 1.0f;
+  const float vdiv = vsc ? ld_const(a.v_scale, g) : 1.0f;
   const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
   const int bs_log2 = a.bs_log2;
   const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
@@ -195,7 +195,19 @@ void decode_split_kernel(const DecodeArgs a) {
   const int qg = lane >> 4;  // MFMA k-group
   const int G = a.num_q_heads / a.num_kv_heads;
   const int rows = a.q_len * G;
-  const int ctx = a.context_lens[b];
+  const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
+  // With pages of >= 64 keys and no window, the block-table entries of the
+  // wave's first two tiles do not depend on the context length: they are
+  // loaded beside it (one round trip before the first K/V load instead of
+  // two). The indices are clamped to the row, and the values are used only
+  // for tiles below the context, where the clamp never acts.
+  [[maybe_unused]] int32_t pre0 = 0, pre1 = 0;
+  if constexpr (UNI) {
+    const int t00 = p * a.part_len + (w << 6);
+    pre0 = ld_const(btb, min(t00 >> a.bs_log2, a.max_blocks - 1));
+    pre1 = ld_const(btb, min((t00 + 256) >> a.bs_log2, a.max_blocks - 1));
+  }
+  const int ctx = ld_const(a.context_lens, b);
   // Rows are causal (window < 0), or see the keys pos - window .. ctx - 1 (the
   // non-causal sliding window). With a window the partitions tile the keys
   // from the first one any row can see, rounded down to a tile: everything
@@ -209,7 +221,6 @@ void decode_split_kernel(const DecodeArgs a) {
   const int bs_log2 = a.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
-  const int32_t* btb = a.block_tables + (int64_t)b * a.max_blocks;
   const int64_t kv_heads = a.num_kv_heads;
   const int first_masked = ctx - a.q_len + 1;  // causal: smallest key some row cannot see
   const int last_lo = ctx - 1 - a.window;      // window: largest first visible key of a row
@@ -224,7 +235,7 @@ void decode_split_kernel(const DecodeArgs a) {
     TilePages pg;
     const int t0 = tile_t0(j);
     if constexpr (UNI) {
-      pg.k = pg.v = btb[t0 >> bs_log2];
+      pg.k = pg.v = ld_const(btb, t0 >> bs_log2);
     } else {
       const int tk = t0 + 16 * (c >> 2), tv = t0 + 16 * qg;
       pg.k = tk < ctx ? btb[tk >> bs_log2] : 0;
@@ -269,7 +280,8 @@ void decode_split_kernel(const DecodeArgs a) {
       }
   };
 
-  const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
+  const float C =
+      a.softmax_scale * (a.k_scale ? ld_const(a.k_scale, g) : 1.0f) * kv_fold<FMT>() * kLog2e;
 
   // Fused quantize-on-write: the work-group whose keys hold some of the new
   // tokens writes them for its KV head before any load (no other work-group
@@ -289,8 +301,9 @@ void decode_split_kernel(const DecodeArgs a) {
   // Start the first tile's traffic before anything else.
   Tile A, B;
   TilePages P0{0, 0}, P1{0, 0};
-  if (J > 0) P0 = pages(0);
-  if (J > 1) P1 = pages(1);
+  const bool pre = UNI && !win;
+  if (J > 0) P0 = pre ? TilePages{pre0, pre0} : pages(0);
+  if (J > 1) P1 = pre ? TilePages{pre1, pre1} : pages(1);
   if (J > 0) load(A, 0, P0);
   (void)B;
 
@@ -415,15 +428,31 @@ void decode_split_kernel(const DecodeArgs a) {
 
   if constexpr (PIPE) {
     // Two-stage pipeline: tile j+1's loads are in flight while tile j is
-    // multiplied; page ids run one more tile ahead. The loop body issues its
-    // loads unconditionally; the last one or two tiles are peeled.
+    // multiplied; page ids run one more tile ahead, and each has a whole
+    // tile's arithmetic to arrive. Scalar page ids (UNI) are issued after the
+    // tile loads before them: scalar loads complete out of order, so using
+    // one waits for every scalar load in flight. Per-lane page ids are vector
+    // loads, which complete in order: they go out before the previous tile's
+    // loads, so waiting for them never waits for that tile. The loop body
+    // issues its loads unconditionally (page-id indices clamped to the
+    // wave's last tile); the last one or two tiles are peeled.
     int j = 0;
     for (; j + 2 < J; j += 2) {
-      P0 = pages(j + 2);
-      load(B, j + 1, P1);
+      if constexpr (UNI) {
+        load(B, j + 1, P1);
+        P0 = pages(j + 2);
+      } else {
+        P0 = pages(j + 2);
+        load(B, j + 1, P1);
+      }
       compute(A, j);
-      if (j + 3 < J) P1 = pages(j + 3);
-      load(A, j + 2, P0);
+      if constexpr (UNI) {
+        load(A, j + 2, P0);
+        P1 = pages(min(j + 3, J - 1));
+      } else {
+        P1 = pages(min(j + 3, J - 1));
+        load(A, j + 2, P0);
+      }
       compute(B, j + 1);
     }
     if (j + 1 < J) {
@@ -437,7 +466,7 @@ void decode_split_kernel(const DecodeArgs a) {
     // One stage; page ids one tile ahead.
     for (int j = 0; j < J; ++j) {
       if (j > 0) load(A, j, P1);
-      if (j + 1 < J) P1 = pages(j + 1);
+      P1 = pages(min(j + 1, J - 1));
       compute(A, j);
     }
   }
@@ -448,7 +477,8 @@ void decode_split_kernel(const DecodeArgs a) {
   // stored here (the combine's arithmetic for one partition), and no combine
   // kernel runs.
   const int64_t P = a.num_parts;
-  [[maybe_unused]] const float vscale = ONEP ? (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>() : 0.0f;
+  [[maybe_unused]] const float vscale =
+      ONEP ? (a.v_scale ? ld_const(a.v_scale, g) : 1.0f) * kv_fold<FMT>() : 0.0f;
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     float lf = l[nb];
@@ -556,7 +586,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
     }
   };
   load_batch(sl);
-  const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
+  const float vscale = (a.v_scale ? ld_const(a.v_scale, g) : 1.0f) * kv_fold<FMT>();
 
   float mloc = kNegInf;
   for (int p = t; p < P; p += kCombineThreads) mloc = fmaxf(mloc, ml[2 * p]);

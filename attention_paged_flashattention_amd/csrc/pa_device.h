@@ -235,4 +235,15 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Load of a value the kernel never writes (block tables, context lengths,
+// scales), through the constant address space. Where the address is
+// wave-uniform this is a scalar load, counted apart from the vector loads:
+// a kernel that also stores to global memory otherwise gets a vector load plus
+// a move to a scalar register, and its wait for that load also waits for every
+// vector load issued before it.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 }  // namespace pa

@@ -131,7 +131,10 @@ pa_status check_common(const void* q, pa_dtype q_dtype, const void* kc, const vo
 int auto_partitions(int batch, int q_len, int hkv, int max_ctx) {
   (void)q_len;
   const int64_t groups = (int64_t)std::max(batch, 1) * hkv;
-  int64_t p = (512 + groups - 1) / groups;               // aim for >= 2 work-groups per CU
+  // Aim for one work-group per CU: fewer, longer partitions stream each
+  // (page, head) run in order, which reads faster from HBM than two
+  // work-groups per CU on half-length runs.
+  int64_t p = (256 + groups - 1) / groups;
   const int64_t max_p = std::max<int64_t>(1, (max_ctx + 255) / 256);  // >= 256 keys each
   p = std::min(p, max_p);
   p = std::max<int64_t>(1, std::min<int64_t>(p, kMaxParts));

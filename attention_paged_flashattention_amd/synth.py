@@ -241,10 +241,11 @@ def long_decode_256k(seed=1005, ctx=262144, partitions=64):
                      meta=dict(partitions=partitions))
 
 
-def headline_decode_128k(seed=1006, ctx=131072, partitions=64):
+def headline_decode_128k(seed=1006, ctx=131072, partitions=32):
     """The 128K FP8 decode headline: the 256K recipe at 131072 tokens
-    (E4M3 per-head scales, 1% x8 K outliers, 64 partitions of 2048 tokens)."""
-    return make_case("decode_128k_e4m3_bs2048_p64", seed, [ctx], 1, 32, 8, 128, 2048,
+    (E4M3 per-head scales, 1% x8 K outliers), split into 32 partitions of
+    4096 tokens (one work-group per CU)."""
+    return make_case("decode_128k_e4m3_bs2048_p32", seed, [ctx], 1, 32, 8, 128, 2048,
                      "f16", "f16", "e4m3", outlier_frac=0.01, outlier_mult=8.0,
                      meta=dict(partitions=partitions))
 

@@ -5,7 +5,7 @@
 
 Prints ONE JSON line. ``value`` is the headline: decode at 128K context over
 an FP8 E4M3 block-paged cache (1 sequence, 32 query / 8 KV heads, head_dim 128,
-2048-token pages, 64 split-KV partitions), in GB/s of algorithmic bytes. One
+2048-token pages, 32 split-KV partitions), in GB/s of algorithmic bytes. One
 step = quantize-on-write of the newest token, the split-KV kernel and the
 log-sum-exp combine -- every step of the decode path -- issued as one
 attn_decode_append_paged call (the write runs inside the split kernel); the
@@ -422,7 +422,7 @@ def empty_section(ev, steps):
     sc = torch.ones((hkv,), dtype=torch.float32, device=dev)
     q = torch.zeros((1, hq, d), dtype=torch.float16, device=dev)
     call = pa.bind_attn_decode_paged(q, kc, vc, "e4m3", bt, ctx, 131072, 0.0884, sc, sc,
-                                     num_partitions=64)[0]
+                                     num_partitions=32)[0]
     stream = torch.cuda.current_stream().cuda_stream
     call()
     torch.cuda.synchronize()
@@ -552,11 +552,11 @@ def main():
     if "decode128k" in sections:
         log("section decode128k")
         res["decode128k"] = decode_like_section(ev, synth.headline_decode_128k(), K, W, 4, 1,
-                                                "decode_128k_e4m3_bs2048_p64", graph=True,
+                                                "decode_128k_e4m3_bs2048_p32", graph=True,
                                                 fused=True)
         log("section decode128k, write and decode as two calls")
         res["decode128k_2call"] = decode_like_section(ev, synth.headline_decode_128k(), K, W, 4, 1,
-                                                      "decode_128k_e4m3_bs2048_p64", graph=True)
+                                                      "decode_128k_e4m3_bs2048_p32", graph=True)
     if "prefill32k" in sections:
         log("section prefill32k")
         res["prefill32k"] = prefill_section(ev, synth.chunked_prefill_32k(), max(10, K // 5),

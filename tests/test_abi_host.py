@@ -192,17 +192,19 @@ def test_supports_table(pa):
 
 
 def test_partitions_and_workspace(pa):
-    # 128K and 256K single-sequence decode: 64 partitions of 2048 / 4096 keys
-    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 131072) == 64
-    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 262144) == 64
-    assert pa.pa_decode_partitions(8, 1, 32, 8, 128, 4096) == 8
-    assert pa.pa_decode_partitions(4, 8, 32, 8, 128, 131072) == 16
+    # one work-group per CU: 128K and 256K single-sequence decode in 32
+    # partitions of 4096 / 8192 keys
+    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 131072) == 32
+    assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 262144) == 32
+    assert pa.pa_decode_partitions(8, 1, 32, 8, 128, 4096) == 4
+    assert pa.pa_decode_partitions(4, 8, 32, 8, 128, 131072) == 8
+    assert pa.pa_decode_partitions(16, 1, 32, 8, 128, 16384) == 2
     assert pa.pa_decode_partitions(1, 1, 32, 8, 128, 100) == 1
-    rows, parts, d = 32, 64, 128
-    ml = rows * parts * 2 * 4
-    want = (ml + 255) // 256 * 256 + rows * parts * d * 4
-    assert pa.pa_workspace_bytes(pa.PA_OP_DECODE, 1, 1, 32, 8, 128, 64, 131072) == want
-    assert pa.pa_workspace_bytes(pa.PA_OP_DECODE, 1, 1, 32, 8, 128, 0, 131072) == want
+    def want(rows, parts, d):
+        ml = rows * parts * 2 * 4
+        return (ml + 255) // 256 * 256 + rows * parts * d * 4
+    assert pa.pa_workspace_bytes(pa.PA_OP_DECODE, 1, 1, 32, 8, 128, 64, 131072) == want(32, 64, 128)
+    assert pa.pa_workspace_bytes(pa.PA_OP_DECODE, 1, 1, 32, 8, 128, 0, 131072) == want(32, 32, 128)
     assert pa.pa_workspace_bytes(pa.PA_OP_PREFILL, 1, 4096, 32, 8, 128, 0, 32768) == 0
     assert pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 16, 131072) == \
         (4 * 8 * 32 * 16 * 2 * 4 + 255) // 256 * 256 + 4 * 8 * 32 * 16 * 128 * 4
@@ -241,10 +243,16 @@ def test_window_workspace_covers_only_the_window(pa):
     context needs a short workspace; a window longer than the context needs
     what the verify call needs."""
     ctx = 131072
-    full = pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 0, ctx)
-    assert pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 0, ctx, 10 ** 6) == full
-    small = pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 0, ctx, 4096)
-    assert 0 < small < full
+    for batch in (1, 4):
+        full = pa.pa_workspace_bytes(pa.PA_OP_VERIFY, batch, 8, 32, 8, 128, 0, ctx)
+        assert pa.pa_window_workspace_bytes(batch, 8, 32, 8, 128, 0, ctx, 10 ** 6) == full
+        small = pa.pa_window_workspace_bytes(batch, 8, 32, 8, 128, 0, ctx, 4096)
+        assert 0 < small <= full
+    # one sequence: 32 partitions over the context, but at most one per 256
+    # keys of the 4096 + 8 + 64 the window's rows span
+    s1 = pa.pa_window_workspace_bytes(1, 8, 32, 8, 128, 0, ctx, 4096)
+    assert s1 == pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 1, 8, 32, 8, 128, 17, ctx)
+    assert s1 < pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 1, 8, 32, 8, 128, 0, ctx)
     # explicit partitions: the same count as verify over the window's span
     assert pa.pa_window_workspace_bytes(4, 8, 32, 8, 128, 2, ctx, 4096) == \
         pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 4, 8, 32, 8, 128, 2, 4096 + 8 + 64)

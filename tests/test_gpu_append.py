@@ -134,7 +134,8 @@ def test_append_equals_write_then_attend(runner, fmt, qdt, q_len, ctx, bs, d, hq
 
 def test_append_headline_128k_step(runner):
     """The 128K decode step in the launch configuration the benchmark times
-    (64 partitions, 2048-token pages): fused call vs write + decode, bitwise."""
+    (32 partitions of 4096 keys, 2048-token pages): fused call vs write +
+    decode, bitwise."""
     from attention_paged_flashattention_amd import pagedattn as pa
     case = synth.headline_decode_128k()
     log(case.name)
