@@ -109,44 +109,59 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   const int64_t t0 = (int64_t)blockIdx.x * kRowTokens;
   const int ntok = (int)min<int64_t>(kRowTokens, a.num_tokens - t0);
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
-  const float kdiv = ksc ? a.k_scale[h] : 1.0f;
-  const float vdiv = vsc ? a.v_scale[h] : 1.0f;
+  const float kdiv = ksc ? ld_const(a.k_scale, h) : 1.0f;
+  const float vdiv = vsc ? ld_const(a.v_scale, h) : 1.0f;
   const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
   const int bs_mask = (1 << a.bs_log2) - 1;
 
-  // every load of the work-group first (the stores below could alias the
-  // sources as far as the compiler knows, so loads interleaved with stores
-  // would each wait for a round trip)
+  // Every load of the work-group first, unconditionally: a chunk of a token
+  // past the end re-reads the last token (its codes are not stored), and the
+  // slots the contiguity check below needs come with them. One wait then
+  // covers all loads, and no load waits behind a store (the stores could
+  // alias the sources as far as the compiler knows).
   constexpr int nf = kRowTokens * cpt;
+  static_assert(nf % 256 == 0, "whole chunks per thread");
+  const int i = threadIdx.x;
   u32x4 kr[kRowIters], vr[kRowIters];
   int64_t sl[kRowIters];
 #pragma unroll
   for (int it = 0; it < kRowIters; ++it) {
-    const int f = threadIdx.x + 256 * it;
+    const int f = i + 256 * it;
     const int tok = f / cpt, ch = f - tok * cpt;
-    if (f < nf && tok < ntok) {
-      const int64_t t = t0 + tok;
-      const int64_t src = (t * a.num_kv_heads + h) * D + ch * 8;
-      kr[it] = ld16(a.key + src);
-      vr[it] = ld16(a.value + src);
-      sl[it] = a.slots[t];
-    }
+    const int64_t t = t0 + min(tok, ntok - 1);
+    const int64_t src = (t * a.num_kv_heads + h) * D + ch * 8;
+    kr[it] = ld16(a.key + src);
+    vr[it] = ld16(a.value + src);
+    sl[it] = a.slots[t];
+  }
+  const int64_t s0 = ld_const(a.slots, t0);
+  const int64_t my_slot = a.slots[t0 + min(i, ntok - 1)];
+  // All loaded values are consumed here (an empty asm statement), so the
+  // compiler waits for them once and cannot sink a load into the conditional
+  // key store that alone uses it. Then all conversions, then the stores.
+#pragma unroll
+  for (int it = 0; it < kRowIters; ++it) asm volatile("" ::"v"(kr[it]), "v"(vr[it]), "v"(sl[it]));
+  asm volatile("" ::"v"(my_slot));
+  u32x4 kc[kRowIters], vc[kRowIters];
+#pragma unroll
+  for (int it = 0; it < kRowIters; ++it) {
+    kc[it] = encode8<ST, FMT>(kr[it], ksc, kdiv, krcp);
+    vc[it] = encode8<ST, FMT>(vr[it], vsc, vdiv, vrcp);
   }
 #pragma unroll
   for (int it = 0; it < kRowIters; ++it) {
-    const int f = threadIdx.x + 256 * it;
+    const int f = i + 256 * it;
     const int tok = f / cpt, ch = f - tok * cpt;
-    if (f >= nf || tok >= ntok) continue;
     const int64_t slot = sl[it];
-    const u32x4 kc = encode8<ST, FMT>(kr[it], ksc, kdiv, krcp);
-    const u32x4 vc = encode8<ST, FMT>(vr[it], vsc, vdiv, vrcp);
-    if (slot >= 0) {
+    if (tok < ntok && slot >= 0) {
       const int64_t ph = (slot >> a.bs_log2) * a.num_kv_heads + h;
       uint8_t* kdst = a.key_cache + (((ph << a.bs_log2) + (slot & bs_mask)) * D + ch * 8) * ES;
-      if constexpr (ES == 2) *reinterpret_cast<u32x4*>(kdst) = kc;
-      else *reinterpret_cast<u32x2*>(kdst) = u32x2{kc.x, kc.y};
+      if constexpr (ES == 2) *reinterpret_cast<u32x4*>(kdst) = kc[it];
+      else *reinterpret_cast<u32x2*>(kdst) = u32x2{kc[it].x, kc[it].y};
     }
-    const uint32_t vw[4] = {vc.x, vc.y, vc.z, vc.w};
+    // value codes to the LDS transpose (cells of tokens past the end are
+    // never read)
+    const uint32_t vw[4] = {vc[it].x, vc[it].y, vc[it].z, vc[it].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint8_t* cell = vt + ((ch * 8 + e) * kRowTokens + tok) * ES;
@@ -156,9 +171,7 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   }
   // one contiguous value block when the 64 slots are consecutive from the
   // start of a value group
-  const int64_t s0 = a.slots[t0];
-  const int i = threadIdx.x;
-  const bool mine = i >= kRowTokens || (i < ntok && a.slots[t0 + i] == s0 + i);
+  const bool mine = i >= kRowTokens || (i < ntok && my_slot == s0 + i);
   const bool block = __syncthreads_and(mine) && ntok == kRowTokens && a.bs_log2 >= 6 &&
                      s0 >= 0 && (s0 & (kRowTokens - 1)) == 0;
   if (block) {
