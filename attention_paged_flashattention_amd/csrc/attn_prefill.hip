@@ -92,12 +92,17 @@ void prefill_kernel(const PrefillArgs a) {
   const int qb = a.q_blocks - 1 - (idx % a.q_blocks);  // heavy tiles first
   const int b = idx / a.q_blocks;
 
-  const int q0 = a.cu_seqlens[b];
-  const int qlen = a.cu_seqlens[b + 1] - q0;
+  // sequence bounds, context length and scales: scalar loads issued together
+  // (read-only here; through the constant address space so that the
+  // compiler does not make them vector loads each waited for in turn)
+  const int q0 = ld_const(a.cu_seqlens, b);
+  const int q1 = ld_const(a.cu_seqlens, b + 1);
+  const int ctx = ld_const(a.context_lens, b);
+  const float kscale = a.k_scale ? ld_const(a.k_scale, g) : 1.0f;
+  const int qlen = q1 - q0;
   const int tok0 = qb * TOK;
   if (tok0 >= qlen) return;
   const int ntok = min(TOK, qlen - tok0);
-  const int ctx = a.context_lens[b];
   const int first_pos = ctx - qlen + tok0;          // position of the first row token
   const int last_pos = first_pos + ntok - 1;
   const int ntiles = last_pos / BN + 1;
@@ -114,7 +119,7 @@ void prefill_kernel(const PrefillArgs a) {
       (const __attribute__((address_space(4))) int32_t*)btb;
   const int64_t kvh = Hkv;
 
-  const float C = a.softmax_scale * (a.k_scale ? a.k_scale[g] : 1.0f) * kv_fold<FMT>() * kLog2e;
+  const float C = a.softmax_scale * kscale * kv_fold<FMT>() * kLog2e;
 
   // This lane's query row (MFMA column): r = 32 w + c32 -> (token, head).
   const int r = w * 32 + c32;
@@ -418,7 +423,7 @@ void prefill_kernel(const PrefillArgs a) {
   // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r].
   l = swap_sum<32>(l);
   if (!rvalid) return;
-  const float vscale = (a.v_scale ? a.v_scale[g] : 1.0f) * kv_fold<FMT>();
+  const float vscale = (a.v_scale ? ld_const(a.v_scale, g) : 1.0f) * kv_fold<FMT>();
   const float f = l > 0.0f ? vscale / l : 0.0f;
   const int64_t obase = ((int64_t)(q0 + tok0 + rtok) * a.num_q_heads + rh) * D;
 #pragma unroll
