@@ -48,21 +48,22 @@ import numpy as np
 from . import paged
 
 
-def _rows_attend(qrows, pos, K, V, scale):
+def _rows_attend(qrows, pos, K, V, scale, probs=True):
     """Causal rows: row r sees keys 0..pos[r]."""
     pos = np.asarray(pos)
-    return _rows_attend_range(qrows, np.zeros_like(pos), pos, K, V, scale)
+    return _rows_attend_range(qrows, np.zeros_like(pos), pos, K, V, scale, probs)
 
 
-def _rows_attend_range(qrows, lo, hi, K, V, scale):
+def _rows_attend_range(qrows, lo, hi, K, V, scale, probs=True):
     """qrows [R, D] float64; row r sees keys lo[r]..hi[r] (inclusive) of the
-    ctx keys in K, V. Returns o [R, D], m [R], l [R], P [R, ctx]."""
+    ctx keys in K, V. Returns o [R, D], m [R], l [R], and P [R, ctx] (None
+    when ``probs`` is false)."""
     R, D = qrows.shape
     ctx = K.shape[0]
     o = np.zeros((R, D))
     m = np.full(R, -np.inf)
     l = np.zeros(R)
-    P = np.zeros((R, ctx))
+    P = np.zeros((R, ctx)) if probs else None
     if ctx == 0:
         return o, m, l, P
     s = scale * (qrows @ K.T)                       # [R, ctx]
@@ -76,7 +77,8 @@ def _rows_attend_range(qrows, lo, hi, K, V, scale):
     o[has] = (p @ V) / l_h[:, None]
     m[has] = m_h
     l[has] = l_h
-    P[has] = p / l_h[:, None]
+    if probs:
+        P[has] = p / l_h[:, None]
     return o, m, l, P
 
 
@@ -139,27 +141,32 @@ def attend(q, q_lens, ctx_lens, k_cache, v_cache, block_tables, fmt,
 
 def attend_rows(q_rows, heads, positions, seq_ctx, k_cache, v_cache, block_table,
                 fmt, num_q_heads, num_kv_heads, softmax_scale, k_scale=None, v_scale=None,
-                window=None):
-    """The same definition for a handful of sampled rows of one sequence:
-    q_rows [R, D], heads [R], positions [R]. Used where the full output is
-    too large for the oracle (rows are independent)."""
+                window=None, row_block=256):
+    """The same definition for selected rows of one sequence: q_rows [R, D],
+    heads [R] (the query head of each row), positions [R]. Each row's result
+    depends only on its own query, head and position, so any subset of rows
+    can be computed on its own; rows of one KV head share that head's gather
+    and are taken ``row_block`` at a time. Returns o [R, D]."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    heads = np.asarray(heads, dtype=np.int64).reshape(-1)
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1)
     G = num_q_heads // num_kv_heads
     scale = np.float64(np.float32(softmax_scale))
     out = np.zeros((len(heads), q_rows.shape[1]))
-    cache = {}
-    for r, (h, pos) in enumerate(zip(heads, positions)):
-        g = int(h) // G
-        if g not in cache:
-            cache[g] = paged.gather(k_cache, v_cache, block_table, seq_ctx, g, fmt,
-                                    k_scale, v_scale)
-        K, V = cache[g]
-        qr = np.asarray(q_rows[r:r + 1], dtype=np.float64)
-        if window is None:
-            ob, _, _, _ = _rows_attend(qr, np.array([pos]), K, V, scale)
-        else:
-            lo, hi = _row_keys(np.array([pos]), seq_ctx, window)
-            ob, _, _, _ = _rows_attend_range(qr, lo, hi, K, V, scale)
-        out[r] = ob[0]
+    kv = heads // G
+    for g in np.unique(kv):
+        idx = np.nonzero(kv == g)[0]
+        K, V = paged.gather(k_cache, v_cache, block_table, seq_ctx, int(g), fmt,
+                            k_scale, v_scale)
+        for i0 in range(0, len(idx), row_block):
+            sel = idx[i0:i0 + row_block]
+            pos = positions[sel]
+            if window is None:
+                ob, _, _, _ = _rows_attend(q_rows[sel], pos, K, V, scale, probs=False)
+            else:
+                lo, hi = _row_keys(pos, seq_ctx, window)
+                ob, _, _, _ = _rows_attend_range(q_rows[sel], lo, hi, K, V, scale, probs=False)
+            out[sel] = ob
     return out
 
 
@@ -180,17 +187,6 @@ def verify(q, ctx_lens, k_cache, v_cache, block_tables, fmt, num_kv_heads,
     o, m, l = attend(q.reshape(B * qlen, Hq, D), [qlen] * B, ctx_lens, k_cache,
                      v_cache, block_tables, fmt, num_kv_heads, softmax_scale,
                      k_scale, v_scale)
-    return o.reshape(B, qlen, Hq, D)
-
-
-def window_attend(q, ctx_lens, k_cache, v_cache, block_tables, fmt, num_kv_heads,
-                  softmax_scale, window, k_scale=None, v_scale=None):
-    """q [B, q_len, Hq, D]: the q_len newest positions of each sequence, each
-    attending non-causally to its sliding window (the draft attention)."""
-    B, qlen, Hq, D = q.shape
-    o, m, l = attend(q.reshape(B * qlen, Hq, D), [qlen] * B, ctx_lens, k_cache, v_cache,
-                     block_tables, fmt, num_kv_heads, softmax_scale, k_scale, v_scale,
-                     window=window)
     return o.reshape(B, qlen, Hq, D)
 
 

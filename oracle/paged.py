@@ -70,6 +70,27 @@ def write(k, v, slot_mapping, k_cache, v_cache, fmt, k_scale=None, v_scale=None)
             v_cache[page, h, off // T, :, off % T] = quantize(v[t, h, :], fmt, vs)
 
 
+def write_tokens(k, v, slot_mapping, k_cache, v_cache, fmt, k_scale=None, v_scale=None,
+                 heads=None):
+    """``write`` for many tokens at once: the same quantization to the same
+    slots, vectorised over the tokens. k, v: [T, H, D]. Without ``heads``,
+    H = Hkv and every KV head is written; with ``heads`` (a list of KV head
+    indices) k[:, i] and v[:, i] hold head ``heads[i]`` and only those heads
+    are written. Slots must be distinct (as for ``write``)."""
+    bs = k_cache.shape[2]
+    T = value_group(bs)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slots >= 0
+    slots = slots[keep]
+    page, off = slots // bs, slots % bs
+    heads = list(range(k.shape[1])) if heads is None else [int(h) for h in heads]
+    for i, h in enumerate(heads):
+        ks = None if k_scale is None else k_scale[h]
+        vs = None if v_scale is None else v_scale[h]
+        k_cache[page, h, off, :] = quantize(k[keep, i, :], fmt, ks)
+        v_cache[page, h, off // T, :, off % T] = quantize(v[keep, i, :], fmt, vs)
+
+
 def dequant(codes, fmt, scale=None):
     """float64 values of cache elements."""
     if fmt == F16:

@@ -13,7 +13,7 @@ import torch
 
 from attention_paged_flashattention_amd import synth
 from oracle import attention
-from tests.oracle_helpers import oracle_cache, q_f32
+from tests.oracle_helpers import oracle_cache, oracle_cache_heads, q_f32  # noqa: F401
 
 TOL = {"f16": 2e-3, "e4m3": 8e-3, "e5m2": 8e-3}
 
@@ -54,29 +54,6 @@ def oracle_full(case, kc=None, vc=None):
                                case.block_tables, case.cache_fmt, case.num_kv_heads,
                                case.softmax_scale, case.k_scale, case.v_scale)
     return o
-
-
-def oracle_cache_heads(case, seqs_heads):
-    """Oracle cache holding only the listed (sequence, KV head) pairs, every
-    other slot poisoned; enough for rows that read those heads."""
-    from oracle import paged
-    fill = {"f16": np.float16(np.nan), "e4m3": synth.POISON["e4m3"],
-            "e5m2": synth.POISON["e5m2"]}[case.cache_fmt]
-    kc, vc = paged.new_caches(case.num_blocks, case.num_kv_heads, case.block_size,
-                              case.head_dim, case.cache_fmt, fill=fill)
-    bs = case.block_size
-    T = paged.value_group(bs)
-    for b, g in seqs_heads:
-        t0, c = int(case.tok_start[b]), int(case.ctx_lens[b])
-        slots = case.slot_mapping[t0:t0 + c]
-        page, off = slots // bs, slots % bs
-        k32 = synth.to_f32(case.k[t0:t0 + c, g, :], case.kv_dtype)
-        v32 = synth.to_f32(case.v[t0:t0 + c, g, :], case.kv_dtype)
-        ks = None if case.k_scale is None else case.k_scale[g]
-        vs = None if case.v_scale is None else case.v_scale[g]
-        kc[page, g, off, :] = paged.quantize(k32, case.cache_fmt, ks)
-        vc[page, g, off // T, :, off % T] = paged.quantize(v32, case.cache_fmt, vs)
-    return kc, vc
 
 
 def oracle_rows(case, kc, vc, b, q_rows_f32, heads, positions, window=None):

@@ -29,7 +29,7 @@ import torch
 
 from attention_paged_flashattention_amd import synth
 from oracle import attention, fp8, paged
-from tests.oracle_helpers import oracle_cache, q_f32, write_tokens
+from tests.oracle_helpers import oracle_cache, q_f32
 
 
 def _case(fmt="e4m3", B=2, ctx=(37, 70), q_len=5, Hq=8, Hkv=2, D=32, bs=16, seed=7,
