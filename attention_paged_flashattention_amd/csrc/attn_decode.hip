@@ -121,7 +121,7 @@ __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, int b, in
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
   const float kdiv = ksc ? ld_const(a.k_scale, g) : 1.0f;
   const float vdiv = vsc ? ld_const(a.v_scale, g) : 1.0f;
-  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
+  const Divisor kd = make_divisor(kdiv), vd = make_divisor(vdiv);
   const int bs_log2 = a.bs_log2;
   const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
   const int64_t T = (int64_t)1 << vg_log2;
@@ -138,8 +138,8 @@ __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, int b, in
     const int64_t page = btb[pos >> bs_log2];
     const int64_t off = pos & ((1 << bs_log2) - 1);
     const int64_t ph = page * a.num_kv_heads + g;
-    const u32x4 codes = isv ? encode8<QT, FMT>(w, vsc, vdiv, vrcp)
-                            : encode8<QT, FMT>(w, ksc, kdiv, krcp);
+    const u32x4 codes = isv ? encode8<QT, FMT>(w, vsc, vd)
+                            : encode8<QT, FMT>(w, ksc, kd);
     if (!isv) {
       uint8_t* kdst = a.key_cache_w + (((ph << bs_log2) + off) * D + ch * 8) * ES;
       if constexpr (ES == 2) *reinterpret_cast<u32x4*>(kdst) = codes;
@@ -623,88 +623,84 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const D
 }
 
 template <int D, int FMT, int QT, int NQB, bool APPEND, bool ONEP>
-static void launch_split_k(const DecodeArgs& a, int batch, hipStream_t stream,
-                           const ProfileEvents& ev) {
+static hipError_t launch_split_k(const DecodeArgs& a, int batch, hipStream_t stream,
+                                 const ProfileEvents& ev) {
   dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)batch);
   if (a.bs_log2 >= 6)
-    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, true, APPEND, ONEP>, grid, dim3(256), 0,
-                  stream, ev, a);
-  else
-    launch_kernel(decode_split_kernel<D, FMT, QT, NQB, false, APPEND, ONEP>, grid, dim3(256), 0,
-                  stream, ev, a);
+    return launch_kernel(decode_split_kernel<D, FMT, QT, NQB, true, APPEND, ONEP>, grid, dim3(256),
+                         0, stream, ev, a);
+  return launch_kernel(decode_split_kernel<D, FMT, QT, NQB, false, APPEND, ONEP>, grid, dim3(256),
+                       0, stream, ev, a);
 }
 
 // One partition (decode and q8-wide verify): the split kernel writes the
 // output and the combine is not launched.
 template <int D, int FMT, int QT, int NQB, bool APPEND>
-static void launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream,
-                             const ProfileEvents& ev) {
+static hipError_t launch_split_app(const DecodeArgs& a, int batch, hipStream_t stream,
+                                   const ProfileEvents& ev) {
   if constexpr (NQB <= 2) {
-    if (a.num_parts == 1) {
-      launch_split_k<D, FMT, QT, NQB, APPEND, true>(a, batch, stream, ev);
-      return;
-    }
+    if (a.num_parts == 1) return launch_split_k<D, FMT, QT, NQB, APPEND, true>(a, batch, stream, ev);
   }
-  launch_split_k<D, FMT, QT, NQB, APPEND, false>(a, batch, stream, ev);
+  return launch_split_k<D, FMT, QT, NQB, APPEND, false>(a, batch, stream, ev);
 }
 
 // The fused write runs in single-block kernels only (the host writes the new
 // tokens with a separate kernel for wider row groups).
 template <int D, int FMT, int QT, int NQB>
-static void launch_split(const DecodeArgs& a, int batch, hipStream_t stream,
-                         const ProfileEvents& ev) {
+static hipError_t launch_split(const DecodeArgs& a, int batch, hipStream_t stream,
+                               const ProfileEvents& ev) {
   if constexpr (NQB == 1) {
-    if (a.k_new != nullptr) {
-      launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream, ev);
-      return;
-    }
+    if (a.k_new != nullptr) return launch_split_app<D, FMT, QT, NQB, true>(a, batch, stream, ev);
   }
-  launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream, ev);
+  return launch_split_app<D, FMT, QT, NQB, false>(a, batch, stream, ev);
 }
 
 template <int D, int FMT, int QT>
-static void launch_split_nqb(const DecodeArgs& a, int batch, int nqb, hipStream_t stream,
-                             const ProfileEvents& ev) {
-  if (nqb == 1) launch_split<D, FMT, QT, 1>(a, batch, stream, ev);
-  else if (nqb == 2) launch_split<D, FMT, QT, 2>(a, batch, stream, ev);
-  else launch_split<D, FMT, QT, 4>(a, batch, stream, ev);
+static hipError_t launch_split_nqb(const DecodeArgs& a, int batch, int nqb, hipStream_t stream,
+                                   const ProfileEvents& ev) {
+  if (nqb == 1) return launch_split<D, FMT, QT, 1>(a, batch, stream, ev);
+  if (nqb == 2) return launch_split<D, FMT, QT, 2>(a, batch, stream, ev);
+  return launch_split<D, FMT, QT, 4>(a, batch, stream, ev);
 }
 
 template <int D, int FMT>
-static void launch_combine(const DecodeArgs& a, int64_t rows, int ot, hipStream_t stream) {
+static hipError_t launch_combine(const DecodeArgs& a, int64_t rows, int ot, hipStream_t stream) {
   dim3 grid((unsigned)rows), block(kCombineThreads);
   const ProfileEvents none{};
-  if (ot == O_F32) launch_kernel(decode_combine_kernel<D, FMT, O_F32>, grid, block, 0, stream, none, a);
-  else if (ot == O_F16) launch_kernel(decode_combine_kernel<D, FMT, O_F16>, grid, block, 0, stream, none, a);
-  else launch_kernel(decode_combine_kernel<D, FMT, O_BF16>, grid, block, 0, stream, none, a);
+  if (ot == O_F32)
+    return launch_kernel(decode_combine_kernel<D, FMT, O_F32>, grid, block, 0, stream, none, a);
+  if (ot == O_F16)
+    return launch_kernel(decode_combine_kernel<D, FMT, O_F16>, grid, block, 0, stream, none, a);
+  return launch_kernel(decode_combine_kernel<D, FMT, O_BF16>, grid, block, 0, stream, none, a);
 }
 
 template <int D>
-static void launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int ot, int nqb,
-                            hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeArgs& a, int batch, int fmt, int qt, int ot,
+                                  int nqb, hipStream_t stream) {
   const ProfileEvents ev = take_profile_events();
+  hipError_t e;
   if (fmt == KV_F16) {
-    launch_split_nqb<D, KV_F16, Q_F16>(a, batch, nqb, stream, ev);
+    e = launch_split_nqb<D, KV_F16, Q_F16>(a, batch, nqb, stream, ev);
   } else if (fmt == KV_E4M3) {
-    if (qt == Q_BF16) launch_split_nqb<D, KV_E4M3, Q_BF16>(a, batch, nqb, stream, ev);
-    else launch_split_nqb<D, KV_E4M3, Q_F16>(a, batch, nqb, stream, ev);
+    e = qt == Q_BF16 ? launch_split_nqb<D, KV_E4M3, Q_BF16>(a, batch, nqb, stream, ev)
+                     : launch_split_nqb<D, KV_E4M3, Q_F16>(a, batch, nqb, stream, ev);
   } else {
-    if (qt == Q_BF16) launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream, ev);
-    else launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream, ev);
+    e = qt == Q_BF16 ? launch_split_nqb<D, KV_E5M2, Q_BF16>(a, batch, nqb, stream, ev)
+                     : launch_split_nqb<D, KV_E5M2, Q_F16>(a, batch, nqb, stream, ev);
   }
-  if (a.num_parts == 1 && nqb <= 2) return;   // the split kernel stored the output
+  if (e != hipSuccess) return e;
+  if (a.num_parts == 1 && nqb <= 2) return hipSuccess;   // the split kernel stored the output
   const int64_t rows = (int64_t)batch * a.q_len * a.num_q_heads;
-  if (fmt == KV_F16) launch_combine<D, KV_F16>(a, rows, ot, stream);
-  else if (fmt == KV_E4M3) launch_combine<D, KV_E4M3>(a, rows, ot, stream);
-  else launch_combine<D, KV_E5M2>(a, rows, ot, stream);
+  if (fmt == KV_F16) return launch_combine<D, KV_F16>(a, rows, ot, stream);
+  if (fmt == KV_E4M3) return launch_combine<D, KV_E4M3>(a, rows, ot, stream);
+  return launch_combine<D, KV_E5M2>(a, rows, ot, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int batch, int head_dim, int fmt, int qt, int ot,
                          int nqb, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  if (head_dim == 64) launch_decode_d<64>(a, batch, fmt, qt, ot, nqb, stream);
-  else launch_decode_d<128>(a, batch, fmt, qt, ot, nqb, stream);
-  return hipGetLastError();
+  if (head_dim == 64) return launch_decode_d<64>(a, batch, fmt, qt, ot, nqb, stream);
+  return launch_decode_d<128>(a, batch, fmt, qt, ot, nqb, stream);
 }
 
 }  // namespace pa

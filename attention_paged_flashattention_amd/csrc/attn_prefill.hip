@@ -126,6 +126,24 @@ void prefill_kernel(const PrefillArgs a) {
   const int rtok = r / G, rh = g * G + r % G;
   const bool rvalid = rtok < ntok;
   const int rpos = first_pos + rtok;
+
+  // A chunk longer than its context (outside the contract: q_len_b <=
+  // context_lens[b]) puts rows before position 0; they see no key. When no
+  // row of this tile sees one, its rows are written as zeros and nothing is
+  // loaded (the block table is never indexed below 0). Rows before position
+  // 0 in a tile that also has later rows get zeros from the masks (no key
+  // passes them, so the row sum stays 0).
+  if (last_pos < 0) {
+    if (rvalid) {
+      const int64_t obase = ((int64_t)(q0 + tok0 + rtok) * a.num_q_heads + rh) * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          store_out<OT>(a.out, obase + 32 * db + 8 * (j >> 2) + 4 * hgrp + (j & 3), 0.0f);
+    }
+    return;
+  }
   OpT qop[KS];
   {
     const uint16_t* qp = a.q + ((int64_t)(q0 + tok0 + rtok) * a.num_q_heads + rh) * D + 8 * hgrp;
@@ -436,34 +454,31 @@ void prefill_kernel(const PrefillArgs a) {
 }
 
 template <int D, int FMT, int QT>
-static void launch_pf(const PrefillArgs& a, int ot, hipStream_t s, const ProfileEvents& ev) {
+static hipError_t launch_pf(const PrefillArgs& a, int ot, hipStream_t s, const ProfileEvents& ev) {
   const unsigned nblk = (unsigned)((int64_t)a.num_kv_heads * a.q_blocks * a.batch);
   dim3 grid(nblk), block(kPrefillThreads);
-  if (ot == O_F32) launch_kernel(prefill_kernel<D, FMT, QT, O_F32>, grid, block, 0, s, ev, a);
-  else if (ot == O_F16) launch_kernel(prefill_kernel<D, FMT, QT, O_F16>, grid, block, 0, s, ev, a);
-  else launch_kernel(prefill_kernel<D, FMT, QT, O_BF16>, grid, block, 0, s, ev, a);
+  if (ot == O_F32) return launch_kernel(prefill_kernel<D, FMT, QT, O_F32>, grid, block, 0, s, ev, a);
+  if (ot == O_F16) return launch_kernel(prefill_kernel<D, FMT, QT, O_F16>, grid, block, 0, s, ev, a);
+  return launch_kernel(prefill_kernel<D, FMT, QT, O_BF16>, grid, block, 0, s, ev, a);
 }
 
 template <int D>
-static void launch_pf_d(const PrefillArgs& a, int fmt, int qt, int ot, hipStream_t s,
-                        const ProfileEvents& ev) {
-  if (fmt == KV_F16) launch_pf<D, KV_F16, Q_F16>(a, ot, s, ev);
-  else if (fmt == KV_E4M3) {
-    if (qt == Q_BF16) launch_pf<D, KV_E4M3, Q_BF16>(a, ot, s, ev);
-    else launch_pf<D, KV_E4M3, Q_F16>(a, ot, s, ev);
-  } else {
-    if (qt == Q_BF16) launch_pf<D, KV_E5M2, Q_BF16>(a, ot, s, ev);
-    else launch_pf<D, KV_E5M2, Q_F16>(a, ot, s, ev);
-  }
+static hipError_t launch_pf_d(const PrefillArgs& a, int fmt, int qt, int ot, hipStream_t s,
+                              const ProfileEvents& ev) {
+  if (fmt == KV_F16) return launch_pf<D, KV_F16, Q_F16>(a, ot, s, ev);
+  if (fmt == KV_E4M3)
+    return qt == Q_BF16 ? launch_pf<D, KV_E4M3, Q_BF16>(a, ot, s, ev)
+                        : launch_pf<D, KV_E4M3, Q_F16>(a, ot, s, ev);
+  return qt == Q_BF16 ? launch_pf<D, KV_E5M2, Q_BF16>(a, ot, s, ev)
+                      : launch_pf<D, KV_E5M2, Q_F16>(a, ot, s, ev);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int fmt, int qt, int ot,
                           hipStream_t stream) {
   if (a.batch == 0 || a.q_blocks == 0) return hipSuccess;
   const ProfileEvents ev = take_profile_events();
-  if (head_dim == 64) launch_pf_d<64>(a, fmt, qt, ot, stream, ev);
-  else launch_pf_d<128>(a, fmt, qt, ot, stream, ev);
-  return hipGetLastError();
+  if (head_dim == 64) return launch_pf_d<64>(a, fmt, qt, ot, stream, ev);
+  return launch_pf_d<128>(a, fmt, qt, ot, stream, ev);
 }
 
 }  // namespace pa

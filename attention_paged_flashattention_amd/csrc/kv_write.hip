@@ -9,7 +9,8 @@
 // context.
 //
 // Quantization: x / scale as the correctly rounded fp32 quotient (from the
-// correctly rounded reciprocal and one fma correction), then the fp32 value to
+// scale's reciprocal and one fma correction where that is exact, a division
+// elsewhere: pa_divide.h), then the fp32 value to
 // FP8 by gfx950's packed conversion after a clamp to the largest finite value
 // (round to nearest even, saturating, sign kept).
 //
@@ -25,12 +26,12 @@ namespace pa {
 
 // 4 source elements (8 bytes) -> 4 FP8 codes.
 template <int ST, int FMT>
-__device__ __forceinline__ uint32_t encode4(u32x2 w, bool scaled, float div, float rdiv) {
+__device__ __forceinline__ uint32_t encode4(u32x2 w, bool scaled, const Divisor& div) {
   float y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float x = src_to_f32<ST>((uint16_t)((i < 2 ? w.x : w.y) >> ((i & 1) * 16)));
-    y[i] = scaled ? div_rn(x, div, rdiv) : x;   // x / div, correctly rounded
+    y[i] = scaled ? div_rn(x, div) : x;   // x / scale, correctly rounded
   }
   return fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]);
 }
@@ -49,7 +50,7 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
   const float kdiv = ksc ? a.k_scale[h] : 1.0f;
   const float vdiv = vsc ? a.v_scale[h] : 1.0f;
-  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
+  const Divisor kd = make_divisor(kdiv), vd = make_divisor(vdiv);
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
@@ -72,9 +73,9 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t t, int h
     for (int i = 0; i < 16; ++i)
       reinterpret_cast<uint16_t*>(vdst)[(int64_t)i * T] = (uint16_t)(vw[i >> 1] >> ((i & 1) * 16));
   } else {
-    const u32x4 k0 = encode8<ST, FMT>(kr0, ksc, kdiv, krcp), k1 = encode8<ST, FMT>(kr1, ksc, kdiv, krcp);
+    const u32x4 k0 = encode8<ST, FMT>(kr0, ksc, kd), k1 = encode8<ST, FMT>(kr1, ksc, kd);
     *reinterpret_cast<u32x4*>(kdst) = u32x4{k0.x, k0.y, k1.x, k1.y};
-    const u32x4 v0 = encode8<ST, FMT>(vr0, vsc, vdiv, vrcp), v1 = encode8<ST, FMT>(vr1, vsc, vdiv, vrcp);
+    const u32x4 v0 = encode8<ST, FMT>(vr0, vsc, vd), v1 = encode8<ST, FMT>(vr1, vsc, vd);
     const uint32_t vw[4] = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
     for (int i = 0; i < 16; ++i) vdst[(int64_t)i * T] = (uint8_t)(vw[i >> 2] >> ((i & 3) * 8));
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
   const float kdiv = ksc ? ld_const(a.k_scale, h) : 1.0f;
   const float vdiv = vsc ? ld_const(a.v_scale, h) : 1.0f;
-  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
+  const Divisor kd = make_divisor(kdiv), vd = make_divisor(vdiv);
   const int bs_mask = (1 << a.bs_log2) - 1;
 
   // Every load of the work-group first, unconditionally: a chunk of a token
@@ -145,8 +146,8 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   u32x4 kc[kRowIters], vc[kRowIters];
 #pragma unroll
   for (int it = 0; it < kRowIters; ++it) {
-    kc[it] = encode8<ST, FMT>(kr[it], ksc, kdiv, krcp);
-    vc[it] = encode8<ST, FMT>(vr[it], vsc, vdiv, vrcp);
+    kc[it] = encode8<ST, FMT>(kr[it], ksc, kd);
+    vc[it] = encode8<ST, FMT>(vr[it], vsc, vd);
   }
 #pragma unroll
   for (int it = 0; it < kRowIters; ++it) {
@@ -225,7 +226,7 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
   const float kdiv = ksc ? a.k_scale[h] : 1.0f;
   const float vdiv = vsc ? a.v_scale[h] : 1.0f;
-  const float krcp = 1.0f / kdiv, vrcp = 1.0f / vdiv;   // correctly rounded reciprocals
+  const Divisor kd = make_divisor(kdiv), vd = make_divisor(vdiv);
   const int64_t slot = DERIVED ? derived_slot(a, t) : a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> a.bs_log2;
@@ -244,8 +245,8 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, int t, int h, int
     vd[2 * T] = (uint16_t)vr.y;
     vd[3 * T] = (uint16_t)(vr.y >> 16);
   } else {
-    *reinterpret_cast<uint32_t*>(kdst) = encode4<ST, FMT>(kr, ksc, kdiv, krcp);
-    const uint32_t vcode = encode4<ST, FMT>(vr, vsc, vdiv, vrcp);
+    *reinterpret_cast<uint32_t*>(kdst) = encode4<ST, FMT>(kr, ksc, kd);
+    const uint32_t vcode = encode4<ST, FMT>(vr, vsc, vd);
 #pragma unroll
     for (int i = 0; i < 4; ++i) vdst[i * T] = (uint8_t)(vcode >> (i * 8));
   }
@@ -279,57 +280,51 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const WriteArgs a) {
 constexpr int64_t kFewTokens = 64;
 
 template <int ST, int FMT>
-static void launch_write(const WriteArgs& a, hipStream_t s, const ProfileEvents& ev) {
+static hipError_t launch_write(const WriteArgs& a, hipStream_t s, const ProfileEvents& ev) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
   const size_t rows_lds = (size_t)a.head_dim * kRowTokens * ES;
   if (a.num_tokens < kFewTokens) {
     const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
-    launch_kernel(kv_write_chunks_kernel<ST, FMT>, dim3((unsigned)((total + 255) / 256)),
-                  dim3(256), 0, s, ev, a);
+    return launch_kernel(kv_write_chunks_kernel<ST, FMT>, dim3((unsigned)((total + 255) / 256)),
+                         dim3(256), 0, s, ev, a);
   } else if (a.head_dim == 64 || a.head_dim == 128) {
     dim3 grid((unsigned)((a.num_tokens + kRowTokens - 1) / kRowTokens), (unsigned)a.num_kv_heads);
     if (a.head_dim == 64)
-      launch_kernel(kv_write_rows_kernel<ST, FMT, 64>, grid, dim3(256), (uint32_t)rows_lds, s, ev, a);
-    else
-      launch_kernel(kv_write_rows_kernel<ST, FMT, 128>, grid, dim3(256), (uint32_t)rows_lds, s, ev, a);
-  } else {
-    dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads);
-    launch_kernel(kv_write_tokens_kernel<ST, FMT>, grid, dim3(256), 0, s, ev, a);
+      return launch_kernel(kv_write_rows_kernel<ST, FMT, 64>, grid, dim3(256), (uint32_t)rows_lds,
+                           s, ev, a);
+    return launch_kernel(kv_write_rows_kernel<ST, FMT, 128>, grid, dim3(256), (uint32_t)rows_lds,
+                         s, ev, a);
   }
+  dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads);
+  return launch_kernel(kv_write_tokens_kernel<ST, FMT>, grid, dim3(256), 0, s, ev, a);
 }
 
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   const ProfileEvents ev = take_profile_events();
-  if (fmt == KV_F16) launch_write<Q_F16, KV_F16>(a, stream, ev);
-  else if (fmt == KV_E4M3) {
-    if (src_is_bf16) launch_write<Q_BF16, KV_E4M3>(a, stream, ev);
-    else launch_write<Q_F16, KV_E4M3>(a, stream, ev);
-  } else {
-    if (src_is_bf16) launch_write<Q_BF16, KV_E5M2>(a, stream, ev);
-    else launch_write<Q_F16, KV_E5M2>(a, stream, ev);
-  }
-  return hipGetLastError();
+  if (fmt == KV_F16) return launch_write<Q_F16, KV_F16>(a, stream, ev);
+  if (fmt == KV_E4M3)
+    return src_is_bf16 ? launch_write<Q_BF16, KV_E4M3>(a, stream, ev)
+                       : launch_write<Q_F16, KV_E4M3>(a, stream, ev);
+  return src_is_bf16 ? launch_write<Q_BF16, KV_E5M2>(a, stream, ev)
+                     : launch_write<Q_F16, KV_E5M2>(a, stream, ev);
 }
 
 template <int ST, int FMT>
-static void launch_append(const WriteArgs& a, hipStream_t s) {
+static hipError_t launch_append(const WriteArgs& a, hipStream_t s) {
   const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_dim / 4);
-  launch_kernel(kv_append_kernel<ST, FMT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                ProfileEvents{}, a);
+  return launch_kernel(kv_append_kernel<ST, FMT>, dim3((unsigned)((total + 255) / 256)),
+                       dim3(256), 0, s, ProfileEvents{}, a);
 }
 
 hipError_t launch_kv_append(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
-  if (fmt == KV_F16) launch_append<Q_F16, KV_F16>(a, stream);
-  else if (fmt == KV_E4M3) {
-    if (src_is_bf16) launch_append<Q_BF16, KV_E4M3>(a, stream);
-    else launch_append<Q_F16, KV_E4M3>(a, stream);
-  } else {
-    if (src_is_bf16) launch_append<Q_BF16, KV_E5M2>(a, stream);
-    else launch_append<Q_F16, KV_E5M2>(a, stream);
-  }
-  return hipGetLastError();
+  if (fmt == KV_F16) return launch_append<Q_F16, KV_F16>(a, stream);
+  if (fmt == KV_E4M3)
+    return src_is_bf16 ? launch_append<Q_BF16, KV_E4M3>(a, stream)
+                       : launch_append<Q_F16, KV_E4M3>(a, stream);
+  return src_is_bf16 ? launch_append<Q_BF16, KV_E5M2>(a, stream)
+                     : launch_append<Q_F16, KV_E5M2>(a, stream);
 }
 
 }  // namespace pa

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_divide.h"
+
 namespace pa {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -104,20 +106,6 @@ __device__ __forceinline__ constexpr float kv_fold() {
   return 1.0f;
 }
 
-// x / s correctly rounded, from r = the correctly rounded 1/s: q = x * r is
-// within an ulp of x / s, the remainder x - s * q is exact under fma, and one
-// correction q + r * (x - s * q) rounded once is the correctly rounded quotient
-// (Markstein's theorem for round-to-nearest, no overflow or underflow in the
-// steps). An exact q (zero remainder, which keeps the sign of a zero x) and a
-// non-finite q (inf x, or a quotient past the fp32 range) are returned as
-// they are. Three operations per element instead of a full division.
-__device__ __forceinline__ float div_rn(float x, float s, float r) {
-  const float q = x * r;
-  const float e = __builtin_fmaf(-q, s, x);
-  const bool keep = e == 0.0f || !__builtin_isfinite(q);
-  return keep ? q : __builtin_fmaf(e, r, q);
-}
-
 // Four fp32 values -> four FP8 codes (bytes 0..3), round to nearest even,
 // saturating, sign kept, by gfx950's packed conversions. The values are first
 // clamped to the format's largest finite value (NaN passes through), so the
@@ -149,7 +137,7 @@ __device__ __forceinline__ float src_to_f32(uint16_t bits) {
 // 8 source elements (one 16-byte chunk) -> 8 cache codes: FP8 in the low 8
 // bytes, or the fp16 elements unchanged.
 template <int ST, int FMT>
-__device__ __forceinline__ u32x4 encode8(u32x4 w, bool scaled, float div, float rdiv) {
+__device__ __forceinline__ u32x4 encode8(u32x4 w, bool scaled, const Divisor& div) {
   if constexpr (FMT == KV_F16) {
     return w;
   } else {
@@ -158,7 +146,7 @@ __device__ __forceinline__ u32x4 encode8(u32x4 w, bool scaled, float div, float 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float x = src_to_f32<ST>((uint16_t)(ww[i >> 1] >> ((i & 1) * 16)));
-      y[i] = scaled ? div_rn(x, div, rdiv) : x;   // x / div, correctly rounded
+      y[i] = scaled ? div_rn(x, div) : x;   // x / scale, correctly rounded
     }
     return u32x4{fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]),
                  fp8x4_from_f32<FMT>(y[4], y[5], y[6], y[7]), 0u, 0u};

@@ -85,18 +85,20 @@ struct ProfileEvents {
 };
 ProfileEvents take_profile_events();
 
-// Launches kernel(a) on stream s. With profiling events pending they are
-// attached to this kernel's own dispatch (hipExtLaunchKernel), so the pair
-// times the kernel alone, without the latency of separate marker packets.
+// Launches kernel(a) on stream s and returns the launch's own status (the
+// caller stops at the first failure; no error state left over from earlier
+// HIP calls is read). With profiling events pending they are attached to this
+// kernel's own dispatch (hipExtLaunchKernel), so the pair times the kernel
+// alone, without the latency of separate marker packets.
 template <typename Arg>
-inline void launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, uint32_t shmem,
-                          hipStream_t s, const ProfileEvents& ev, const Arg& a) {
+[[nodiscard]] inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block,
+                                              uint32_t shmem, hipStream_t s,
+                                              const ProfileEvents& ev, const Arg& a) {
   void* args[] = {const_cast<Arg*>(&a)};
   const void* fn = reinterpret_cast<const void*>(kernel);
   if (ev.start && ev.stop)
-    (void)hipExtLaunchKernel(fn, grid, block, args, shmem, s, ev.start, ev.stop, 0);
-  else
-    (void)hipLaunchKernel(fn, grid, block, args, shmem, s);
+    return hipExtLaunchKernel(fn, grid, block, args, shmem, s, ev.start, ev.stop, 0);
+  return hipLaunchKernel(fn, grid, block, args, shmem, s);
 }
 
 hipError_t launch_kv_write(const WriteArgs& a, int src_is_bf16, int fmt, hipStream_t stream);

@@ -516,17 +516,21 @@ PA_API int pa_supports(int op, pa_dtype q_dtype, pa_dtype cache_dtype, int head_
 
 PA_API pa_status pa_validate_tables(const int32_t* block_tables, int batch, int max_blocks_per_seq,
                                     const int32_t* context_lens, int max_context_len,
-                                    int block_size, int64_t num_blocks, void* stream) {
+                                    int block_size, int64_t num_blocks,
+                                    const int32_t* cu_seqlens_q, void* stream) {
   if (!block_tables || !context_lens || batch < 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
       num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: bad arguments");
   if (batch == 0) return ok();
   std::vector<int32_t> bt((size_t)batch * max_blocks_per_seq), cl((size_t)batch);
+  std::vector<int32_t> cu(cu_seqlens_q ? (size_t)batch + 1 : 0);
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e == hipSuccess)
     e = hipMemcpy(bt.data(), block_tables, bt.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e == hipSuccess)
     e = hipMemcpy(cl.data(), context_lens, cl.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && cu_seqlens_q)
+    e = hipMemcpy(cu.data(), cu_seqlens_q, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_status(e, "pa_validate_tables");
   const int64_t cap = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
   for (int b = 0; b < batch; ++b) {
@@ -539,6 +543,19 @@ PA_API pa_status pa_validate_tables(const int32_t* block_tables, int batch, int 
       if (id < 0 || id >= num_blocks)
         return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: block_tables[%d][%d] = %d outside [0, %lld)",
                     b, k, id, (long long)num_blocks);
+    }
+  }
+  if (cu_seqlens_q) {
+    if (cu[0] != 0)
+      return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: cu_seqlens_q[0] = %d, not 0", cu[0]);
+    for (int b = 0; b < batch; ++b) {
+      const int64_t q_len = (int64_t)cu[b + 1] - cu[b];
+      if (q_len < 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_validate_tables: cu_seqlens_q decreases at %d", b + 1);
+      if (q_len > cl[b])
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_validate_tables: sequence %d has %lld new queries but context_lens %d",
+                    b, (long long)q_len, cl[b]);
     }
   }
   return ok();

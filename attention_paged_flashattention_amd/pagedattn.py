@@ -68,7 +68,7 @@ _lib.pa_supports.argtypes = [_i32] * 8
 _lib.pa_supports.restype = _i32
 _lib.pa_last_error.restype = ctypes.c_char_p
 _lib.pa_version.restype = ctypes.c_char_p
-_lib.pa_validate_tables.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i64, _vp]
+_lib.pa_validate_tables.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i64, _vp, _vp]
 _lib.pa_profile_next_call.argtypes = [_vp, _vp]
 _lib.pa_profile_next_call.restype = None
 for _name in ("kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
@@ -377,8 +377,9 @@ def pa_profile_next_call(start_event, stop_event):
 
 
 def pa_validate_tables(block_tables, context_lens, max_context_len, block_size, num_blocks,
-                       stream=None):
+                       cu_seqlens_q=None, stream=None):
+    cu = None if cu_seqlens_q is None else _ptr(cu_seqlens_q)
     st = _lib.pa_validate_tables(_ptr(block_tables), block_tables.shape[0], block_tables.shape[1],
                                  _ptr(context_lens), int(max_context_len), int(block_size),
-                                 int(num_blocks), _stream(block_tables.device, stream))
+                                 int(num_blocks), cu, _stream(block_tables.device, stream))
     _check(st)

@@ -277,6 +277,17 @@ def chunked_prefill_64k(seed=1009, total=65536, chunk=4096):
                      32, 8, 128, 2048, "bf16", "bf16", "e4m3", meta=dict(chunk=chunk))
 
 
+def chunked_prefill_long(total=131072, chunk=4096, seed=None):
+    """The 32K chunked-prefill recipe to 131072 (seed 1011) or 262144 (seed
+    1012) tokens, 2048-token pages (64 or 128), run in 4096- or 8192-token
+    chunks (the 4096 / 8192 prefill budgets of the long-context profile)."""
+    if seed is None:
+        seed = {131072: 1011, 262144: 1012}[total]
+    return make_case(f"prefill{total // 1024}k_chunk{chunk // 1024}k_bf16_e4m3_bs2048", seed,
+                     [total], [total], 32, 8, 128, 2048, "bf16", "bf16", "e4m3",
+                     meta=dict(chunk=chunk))
+
+
 def window_draft_q8(seed=1010, ctx=131072, window=4096, batch=4):
     """Draft attention: 4 sequences, blocks of 8 new queries each attending
     non-causally to a 4096-key sliding window (plus the later keys of their
@@ -298,5 +309,7 @@ WORKLOADS = {
     "b16": batched_decode_e5m2_16k,
     "q16": verify_q16_128k,
     "64k": chunked_prefill_64k,
+    "128k": lambda chunk=4096: chunked_prefill_long(131072, chunk),
+    "256k": lambda chunk=4096: chunked_prefill_long(262144, chunk),
     "win": window_draft_q8,
 }

@@ -135,6 +135,10 @@ PA_API pa_status kv_cache_write_fp8(
  *                sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
  *   cu_seqlens_q [batch + 1] int32, cu_seqlens_q[0] = 0, non-decreasing;
  *                each q_len_b <= max_q_len (host) and <= context_lens[b]
+ *                (the chunk is written before it is attended; a longer chunk
+ *                is outside the contract, yet its rows before position 0 are
+ *                written as zeros and nothing outside the sequence's pages is
+ *                read; pa_validate_tables checks these bounds)
  *   block_tables [batch][max_blocks_per_seq] int32 physical page ids
  *   context_lens [batch] int32, keys of sequence b including its new chunk
  *   k_scale, v_scale [num_kv_heads] float32 (see kv_cache_write_fp8)
@@ -276,29 +280,58 @@ PA_API pa_status attn_window_paged(
     void* out, pa_dtype out_dtype, void* stream);
 
 /* Bytes of workspace attn_window_paged needs for these arguments
- * (num_partitions = 0 means automatic); 0 for invalid arguments. */
+ * (num_partitions = 0 means automatic); 0 for invalid arguments. Host-only
+ * arithmetic, no device access. The caller owns the workspace, as the engine
+ * of the pages owns and releases its attention workspaces ("1Cat-vLLM 1.5.0"
+ * RELEASE notes, "Reliability and correctness fixes", "Runtime and API
+ * stability": shutdown releases the SM70 global workspaces); the partitions
+ * cover only the keys the window can see ("Flash-V100 long-context
+ * improvements": prefix tiles outside the window are skipped). */
 PA_API size_t pa_window_workspace_bytes(int batch, int q_len, int num_q_heads,
                                         int num_kv_heads, int head_dim, int num_partitions,
                                         int max_context_len, int window_left);
 
-/* Partition count that num_partitions = 0 selects for decode/verify (host). */
+/* Partition count that num_partitions = 0 selects for decode/verify (host
+ * arithmetic, no device access): the split of the long-context decode route
+ * ("1Cat-vLLM 1.5.0" RELEASE notes, "Flash-V100 long-context improvements":
+ * long E4M3 decode routing at 128K/256K), here one work-group per compute
+ * unit and at least 256 keys per partition. Returns 0 for invalid
+ * arguments. */
 PA_API int pa_decode_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads,
                                 int head_dim, int max_context_len);
 
 /* Bytes of workspace attn_decode_paged / attn_verify_paged need (0 for the
- * write and prefill ops). num_partitions = 0 means automatic. Returns 0 for
- * invalid arguments. */
+ * write and prefill ops): one (max, sum) pair and one partial output row per
+ * (query row, partition) of the split-KV decode ("1Cat-vLLM 1.5.0" RELEASE
+ * notes, "Flash-V100 long-context improvements": long-context decode routing).
+ * num_partitions = 0 means automatic. Host-only arithmetic; the caller owns
+ * the workspace ("Reliability and correctness fixes", "Runtime and API
+ * stability": the engine releases its attention workspaces itself). Returns 0
+ * for invalid arguments. */
 PA_API size_t pa_workspace_bytes(int op, int batch, int q_len, int num_q_heads,
                                  int num_kv_heads, int head_dim, int num_partitions,
                                  int max_context_len);
 
-/* 1 if a kernel covers this combination, else 0. q_len is the per-sequence
- * query count (1 for decode, the verify or window block width, the chunk for
- * prefill). */
+/* 1 if a kernel covers this combination, else 0: the capability check a
+ * caller makes before dispatch so that it can fall back for this one operator
+ * ("1Cat-vLLM 1.5.0" RELEASE notes, "Reliability and correctness fixes",
+ * "Runtime and API stability": q16 verification checks the grouped
+ * verifier's capability before dispatch and q8-only builds fall back safely;
+ * "Production DFlash2 on V100": each verifier operator checks its dtype, KV
+ * format and live batch shape and falls back independently). The attention
+ * calls make the same check and return PA_ERR_UNSUPPORTED when it fails.
+ * q_len is the per-sequence query count (1 for decode, the verify or window
+ * block width, the chunk for prefill). Host-only. */
 PA_API int pa_supports(int op, pa_dtype q_dtype, pa_dtype cache_dtype, int head_dim,
                        int num_q_heads, int num_kv_heads, int block_size, int q_len);
 
-/* Description of the last error on the calling thread ("" after success). */
+/* Description of the last error on the calling thread ("" after success):
+ * the reason behind a PA_ERR_* status, so that a caller that falls back for
+ * one operator can report why ("Production DFlash2 on V100": operators fall
+ * back independently when their local contract is not met; "SM70 release
+ * profile and acceleration status": disabled paths are reported with a
+ * reason). The string is owned by the library and valid until the thread's
+ * next call. */
 PA_API const char* pa_last_error(void);
 
 /* Library version string. */
@@ -317,15 +350,25 @@ PA_API const char* pa_version(void);
 PA_API void pa_profile_next_call(void* start_event, void* stop_event);
 
 /*
- * Debug check, synchronous, never on the hot path: copies context_lens and
- * block_tables to the host (after synchronizing `stream`) and verifies
- * 0 <= context_lens[b] <= min(max_context_len, max_blocks_per_seq *
- * block_size) and 0 <= every used block id < num_blocks.
+ * Debug check, synchronous, never on the hot path: copies context_lens,
+ * block_tables and (when not NULL) cu_seqlens_q to the host (after
+ * synchronizing `stream`) and verifies 0 <= context_lens[b] <=
+ * min(max_context_len, max_blocks_per_seq * block_size), that every block id
+ * a visible token uses is a physical page id in [0, num_blocks) ("1Cat-vLLM
+ * 1.5.0" RELEASE notes, "Reliability and correctness fixes": block tables use
+ * physical page units), and, for a prefill batch, that cu_seqlens_q starts at
+ * 0, never decreases and gives each chunk q_len_b <= context_lens[b] (a chunk
+ * is written before it is attended). The device-resident values the
+ * attention calls take as preconditions are exactly these. Returns
+ * PA_ERR_INVALID_ARG naming the first violation, PA_ERR_HIP if a copy fails.
+ *
+ *   cu_seqlens_q  [batch + 1] int32 (device) or NULL to skip that check
  */
 PA_API pa_status pa_validate_tables(const int32_t* block_tables, int batch,
                                     int max_blocks_per_seq, const int32_t* context_lens,
                                     int max_context_len, int block_size,
-                                    int64_t num_blocks, void* stream);
+                                    int64_t num_blocks, const int32_t* cu_seqlens_q,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -295,3 +295,40 @@ def test_append_rejects_before_launch(pa, q_len, kw, status):
 def test_append_batch_zero_is_a_noop(pa):
     assert _call_append(pa, 8, batch=0) == 0
     assert pa.pa_last_error() == ""
+
+
+def _no_device():
+    """True where no GPU is present (checked without initialising HIP):
+    valid argument sets then reach the launch, which must fail cleanly."""
+    import torch
+    return not os.path.exists("/dev/kfd") and torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_device(), reason="launches with fake pointers need a GPU-less host")
+def test_valid_calls_without_a_device_report_the_launch_error(pa):
+    """Arguments that pass every host check reach the kernel launch; with no
+    device the launch fails and the call returns PA_ERR_HIP with a message.
+    The status is this call's own: an invalid call right after it reports
+    PA_ERR_INVALID_ARG, and a no-op call reports PA_OK."""
+    L = pa.lib()
+    calls = {
+        "decode": lambda: _call_decode(pa),
+        "decode_e5m2_no_scales": lambda: _call_decode(pa, cache_dtype=4, ks=NUL, vs=NUL),
+        "verify_q8": lambda: _call_verify(pa, 8),
+        "verify_q16": lambda: _call_verify(pa, 16),
+        "window": lambda: _call_window(pa, 8, 16),
+        "append_q1": lambda: _call_append(pa, 1),
+        "append_q8": lambda: _call_append(pa, 8),
+        "write": lambda: L.kv_cache_write_fp8(FAKE, FAKE, 0, FAKE, 10, FAKE, FAKE, 3, 4, 16, 2, 128,
+                                              FAKE, FAKE, NUL),
+        "prefill": lambda: L.attn_prefill_paged(FAKE, 1, FAKE, 1, 64, 64, FAKE, FAKE, 3, 2048, 4,
+                                                FAKE, 2, FAKE, 4096, 32, 8, 128, FAKE, FAKE, 0.088,
+                                                FAKE, 2, NUL),
+    }
+    for name, call in calls.items():
+        assert call() == pa.PA_ERR_HIP, name
+        msg = pa.pa_last_error()
+        assert msg != "", name
+        assert _call_decode(pa, q=NUL) == pa.PA_ERR_INVALID_ARG, name
+        assert _call_decode(pa, batch=0) == pa.PA_OK, name
+        assert pa.pa_last_error() == "", name

@@ -73,7 +73,13 @@ def test_write_bit_exact(runner, fmt, src, bs, D, ctx):
 
 WRITE_SCALES = [("e4m3", 1.0), ("e4m3", 0.0105), ("e4m3", 7.0), ("e4m3", 13.0),
                 ("e4m3", 0.2987244725227356), ("e4m3", 3.1415927410125732e-3),
-                ("e5m2", None), ("e5m2", 0.37)]
+                ("e5m2", None), ("e5m2", 0.37),
+                # scales at the ends of the float32 range: subnormal scales, a
+                # reciprocal that overflows (2^-130, 2^-149) or is subnormal
+                # (2^127): the quotient falls back to a plain division there
+                ("e4m3", 2.0 ** -149), ("e4m3", 2.0 ** -130), ("e4m3", 2.0 ** -126),
+                ("e4m3", 2.0 ** 100), ("e4m3", 2.0 ** 127), ("e4m3", 1.9 * 2.0 ** 127),
+                ("e5m2", 2.0 ** -140), ("e5m2", 1.5 * 2.0 ** 126)]
 
 
 def _all_patterns(src):
@@ -307,6 +313,37 @@ def test_prefill_batched_varlen(runner):
     check_close(out, ref, "e4m3", "prefill varlen f32")
 
 
+@pytest.mark.parametrize("bs", [16, 2048])
+def test_prefill_chunk_longer_than_context(runner, bs):
+    """Chunks longer than their context (outside the contract): rows before
+    position 0 see no key and come back as zeros, rows at position >= 0 match
+    the oracle, and nothing outside the sequences' block-table rows is read
+    (an empty context's row holds only padding). Tiles wholly before position
+    0, tiles that straddle it, and a sequence with no key at all."""
+    case = _mk("e4m3", 3, (40, 0, 600), 1, 32, 8, 128, bs, "bf16")
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    qlens = [300, 100, 200]
+    rng = np.random.default_rng(8)
+    q32 = rng.standard_normal((sum(qlens), 32, 128)).astype(np.float32)
+    qb = synth.round_to(q32, "bf16")
+    from attention_paged_flashattention_amd.runner import upload16
+    qt = upload16(qb, "bf16", "cuda:0")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32, device="cuda:0")
+    log(f"prefill chunks longer than their context: bs={bs} q_lens={qlens} ctx={case.ctx_lens.tolist()}")
+    out = dc.prefill(qt, cu, max(qlens), dc.ctx_lens, int(case.ctx_lens.max()),
+                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    from oracle import attention
+    kc, vc = oracle_cache(case)
+    ref, _, _ = attention.attend(synth.to_f32(qb, "bf16"), qlens, case.ctx_lens, kc, vc,
+                                 case.block_tables, "e4m3", 8, case.softmax_scale, case.k_scale,
+                                 case.v_scale)
+    assert np.all(ref[:260] == 0) and np.all(ref[300:400] == 0)
+    check_close(out, ref, "e4m3", "prefill q_len > ctx f32")
+    assert torch.all(out[:260] == 0).item() and torch.all(out[300:400] == 0).item()
+
+
 def test_prefill_output_dtypes(runner):
     case = _mk("e4m3", 1, (500,), 500, 32, 8, 128, 16, "bf16")
     dc = runner.DeviceCase(case)
@@ -437,6 +474,23 @@ def test_validate_tables(runner):
     cl = dc.ctx_lens.clone()
     cl[2] = dc.max_ctx + 1                     # longer than max_context_len
     rejects(dc.block_tables, cl, what="context_lens[2]")
+    # prefill chunk bounds: each chunk no longer than its context
+    dev = dc.block_tables.device
+
+    def cu(*v):
+        return torch.tensor(v, dtype=torch.int32, device=dev)
+    pa.pa_validate_tables(dc.block_tables, dc.ctx_lens, dc.max_ctx, bs, nb,
+                          cu_seqlens_q=cu(0, 100, 117, 117))
+
+    def rejects_cu(c, what):
+        with pytest.raises(pa.PagedAttnError) as e:
+            pa.pa_validate_tables(dc.block_tables, dc.ctx_lens, dc.max_ctx, bs, nb, cu_seqlens_q=c)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
+        assert what in str(e.value), str(e.value)
+    rejects_cu(cu(0, 101, 117, 117), "sequence 0 has 101 new queries")
+    rejects_cu(cu(0, 10, 8, 8), "decreases")
+    rejects_cu(cu(1, 10, 20, 20), "cu_seqlens_q[0]")
+    rejects_cu(cu(0, 10, 20, 21), "sequence 2 has 1 new queries")
     cl = dc.ctx_lens.clone()
     cl[1] = -3
     rejects(dc.block_tables, cl, what="context_lens[1]")

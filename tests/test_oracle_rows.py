@@ -169,3 +169,27 @@ def test_oracle_cache_heads_matches_per_token_write():
         f = attention.attend_rows(qr, heads, [c - 1] * 2, c, kf, vf, case.block_tables[b],
                                   "e4m3", 8, 4, case.softmax_scale, case.k_scale, case.v_scale)
         assert np.array_equal(a, f)
+
+
+def test_oracle_pool_matches_attend():
+    """The worker pool (shared memory-mapped cache, one process per piece of
+    (sequence, KV head) work) returns exactly the oracle's rows: the cache it
+    builds is byte-identical to oracle_cache, and its rows equal attend."""
+    from tests.oracle_pool import OraclePool, row_tasks
+    case = _case("e4m3", (45, 77), 5, 8, 2, bs=16)
+    kc, vc = oracle_cache(case)
+    ref, _, _ = attention.attend(q_f32(case), case.q_lens, case.ctx_lens, kc, vc,
+                                 case.block_tables, "e4m3", 2, case.softmax_scale,
+                                 case.k_scale, case.v_scale)
+    with OraclePool(case, workers=2, tmp_root=None) as pool:
+        pairs = [(b, g) for b in range(2) for g in range(2)]
+        pool.build(pairs, pieces=3)
+        built_k = np.load(pool.dir + "/kc.npy")
+        built_v = np.load(pool.dir + "/vc.npy")
+        assert np.array_equal(built_k, kc) and np.array_equal(built_v, vc)
+        got = np.full_like(ref, np.nan)
+        for b, g in pairs:
+            tasks, index = row_tasks(case, b, g, np.arange(5), split=2)
+            for rows, (t, h) in zip(pool.run(tasks), index):
+                got[b * 5 + t, h] = rows
+    assert np.array_equal(got, ref) or np.max(np.abs(got - ref)) < 1e-13
