@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -163,6 +164,40 @@ size_t ws_bytes(int64_t rows, int parts, int head_dim) {
   return ml_al + (size_t)rows * parts * head_dim * sizeof(float);
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of attn_verify_paged_noalloc: the split-KV partials live in this
+// file-scope device array instead of a caller's workspace. Each GPU holds its
+// own copy (at its own address) until the process ends. In host code the name
+// `scratch` is only a host-side stand-in: every use goes through the device
+// address that hipGetSymbolAddress returns for the current device, looked up
+// once per device and kept in g_scratch.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device (set-up on first use).
+pa_status scratch_ptr(const char* name, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device index %d out of range", name, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", name, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return PA_OK;
+}
+
 pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int batch, int q_len,
                       const void* kc, const void* vc, pa_dtype cache_dtype, int block_size,
                       int64_t num_blocks, const int32_t* block_tables, int max_blocks,
@@ -170,7 +205,8 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
                       int head_dim, const float* k_scale, const float* v_scale,
                       float softmax_scale, int num_partitions, void* workspace,
                       size_t workspace_bytes, void* out, pa_dtype out_dtype, void* stream,
-                      int window = -1, const void* k_new = nullptr, const void* v_new = nullptr) {
+                      int window = -1, const void* k_new = nullptr, const void* v_new = nullptr,
+                      bool use_scratch = false) {
   if (batch < 0) return fail(PA_ERR_INVALID_ARG, "%s: batch must be >= 0", name);
   if (q_len <= 0) return fail(PA_ERR_INVALID_ARG, "%s: q_len must be positive", name);
   if (num_partitions < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_partitions must be >= 0", name);
@@ -193,6 +229,15 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
   partition_shape(req, span, &part_len, &parts);
   const int64_t rows = (int64_t)batch * q_len * hq;
   const size_t need = ws_bytes(rows, parts, head_dim);
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "%s: needs %zu bytes of partials, more than the %zu-byte static scratch "
+                  "(use attn_verify_paged with a workspace)", name, need, kScratchBytes);
+    pa_status sst = scratch_ptr(name, &workspace);
+    if (sst != PA_OK) return sst;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace) return fail(PA_ERR_INVALID_ARG, "%s: workspace is null", name);
   if (workspace_bytes < need)
     return fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu needed",
@@ -413,6 +458,23 @@ PA_API pa_status attn_verify_paged(const void* q, pa_dtype q_dtype, int batch, i
                      context_lens, max_context_len, num_q_heads, num_kv_heads, head_dim, k_scale,
                      v_scale, softmax_scale, num_partitions, workspace, workspace_bytes, out,
                      out_dtype, stream);
+}
+
+PA_API pa_status attn_verify_paged_noalloc(const void* q, pa_dtype q_dtype, int batch, int q_len,
+                                           const void* key_cache, const void* value_cache,
+                                           pa_dtype cache_dtype, int block_size,
+                                           int64_t num_blocks, const int32_t* block_tables,
+                                           int max_blocks_per_seq, const int32_t* context_lens,
+                                           int max_context_len, int num_q_heads,
+                                           int num_kv_heads, int head_dim, const float* k_scale,
+                                           const float* v_scale, float softmax_scale,
+                                           int num_partitions, void* out, pa_dtype out_dtype,
+                                           void* stream) {
+  return decode_like("attn_verify_paged_noalloc", q, q_dtype, batch, q_len, key_cache,
+                     value_cache, cache_dtype, block_size, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_q_heads, num_kv_heads,
+                     head_dim, k_scale, v_scale, softmax_scale, num_partitions, nullptr, 0, out,
+                     out_dtype, stream, -1, nullptr, nullptr, true);
 }
 
 PA_API pa_status attn_window_paged(const void* q, pa_dtype q_dtype, int batch, int q_len,

@@ -25,7 +25,8 @@ CACHE_DTYPES = {"f16": PA_F16, "e4m3": PA_FP8_E4M3, "e5m2": PA_FP8_E5M2}
 TORCH_DTYPES = {torch.float16: PA_F16, torch.bfloat16: PA_BF16, torch.float32: PA_F32}
 
 EXPORTS = ["kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
-           "attn_verify_paged", "attn_decode_append_paged", "attn_window_paged",
+           "attn_verify_paged", "attn_verify_paged_noalloc", "attn_decode_append_paged",
+           "attn_window_paged",
            "pa_window_workspace_bytes",
            "pa_decode_partitions", "pa_workspace_bytes",
            "pa_supports", "pa_last_error", "pa_version", "pa_validate_tables",
@@ -57,6 +58,9 @@ _DECODE_TAIL = [_vp, _vp, _i32, _i32, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _i
 _lib.attn_decode_paged.argtypes = [_vp, _i32, _i32] + _DECODE_TAIL
 _lib.attn_verify_paged.argtypes = [_vp, _i32, _i32, _i32] + _DECODE_TAIL
 _lib.attn_window_paged.argtypes = [_vp, _i32, _i32, _i32, _i32] + _DECODE_TAIL
+# the same tail without (workspace, workspace_bytes)
+_lib.attn_verify_paged_noalloc.argtypes = [_vp, _i32, _i32, _i32] + _DECODE_TAIL[:16] + \
+    _DECODE_TAIL[18:]
 _lib.attn_decode_append_paged.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp] + _DECODE_TAIL
 _lib.pa_window_workspace_bytes.argtypes = [_i32] * 8
 _lib.pa_window_workspace_bytes.restype = _sz
@@ -72,7 +76,8 @@ _lib.pa_validate_tables.argtypes = [_vp, _i32, _i32, _vp, _i32, _i32, _i64, _vp,
 _lib.pa_profile_next_call.argtypes = [_vp, _vp]
 _lib.pa_profile_next_call.restype = None
 for _name in ("kv_cache_write_fp8", "attn_prefill_paged", "attn_decode_paged",
-              "attn_verify_paged", "attn_decode_append_paged", "attn_window_paged",
+              "attn_verify_paged", "attn_verify_paged_noalloc", "attn_decode_append_paged",
+              "attn_window_paged",
               "pa_validate_tables"):
     getattr(_lib, _name).restype = _i32
 
@@ -319,6 +324,30 @@ def attn_verify_paged(q, key_cache, value_cache, cache_dtype, block_tables, cont
                         value_cache, cache_dtype, block_tables, context_lens, max_context_len,
                         softmax_scale, k_scale, v_scale, num_partitions, workspace, out,
                         out_dtype, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # the static scratch of attn_verify_paged_noalloc
+
+
+def attn_verify_paged_noalloc(q, key_cache, value_cache, cache_dtype, block_tables,
+                              context_lens, max_context_len, softmax_scale, out, k_scale=None,
+                              v_scale=None, num_partitions=0, stream=None):
+    """attn_verify_paged with the partials in the library's static device
+    scratch: q [B, q_len, Hq, D]; out [B, q_len, Hq, D] is caller-allocated
+    (F32, F16 or BF16). No device memory is allocated by this call."""
+    _need(q, "q", (torch.float16, torch.bfloat16), 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(out, "out", (torch.float32, torch.float16, torch.bfloat16))
+    batch, q_len, hq, d = q.shape
+    nb, hkv, bs, _ = key_cache.shape
+    _check(_lib.attn_verify_paged_noalloc(
+        _ptr(q), TORCH_DTYPES[q.dtype], batch, q_len, _ptr(key_cache), _ptr(value_cache),
+        _cache_dtype(cache_dtype), bs, nb, _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), int(max_context_len), hq, hkv, d, _ptr(k_scale), _ptr(v_scale),
+        float(softmax_scale), int(num_partitions), _ptr(out), TORCH_DTYPES[out.dtype],
+        _stream(q.device, stream)))
+    return out
 
 
 def attn_decode_append_paged(q, key_new, value_new, key_cache, value_cache, cache_dtype,

@@ -207,6 +207,37 @@ PA_API pa_status attn_verify_paged(
     void* out, pa_dtype out_dtype, void* stream);
 
 /*
+ * attn_verify_paged without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation. Same arguments, kernels and
+ * results as attn_verify_paged (bit for bit, q_len = 1 is decode), but the
+ * split-KV partials go to a static device array of 16 MiB that the library
+ * holds on each GPU it runs on until the process ends. This call allocates
+ * nothing and frees nothing (the array's device address is looked up once per
+ * device, on the first call with that device current).
+ *
+ *   Limit: the partials need pa_workspace_bytes(PA_OP_VERIFY, batch, q_len,
+ *          num_q_heads, num_kv_heads, head_dim, num_partitions,
+ *          max_context_len) bytes; a call needing more than 16 MiB (16777216)
+ *          returns PA_ERR_UNSUPPORTED before launching anything (the 128K
+ *          headline decode needs 0.5 MiB, 4 x 128K q16 verify 8.5 MiB).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *          last call's partials (every value read is written first by the same
+ *          call, so nothing needs clearing). Calls that overlap on one GPU --
+ *          on different streams, or from several threads without ordering --
+ *          race on the array and may return wrong results; order them.
+ */
+PA_API pa_status attn_verify_paged_noalloc(
+    const void* q, pa_dtype q_dtype, int batch, int q_len,
+    const void* key_cache, const void* value_cache, pa_dtype cache_dtype,
+    int block_size, int64_t num_blocks,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int max_context_len,
+    int num_q_heads, int num_kv_heads, int head_dim,
+    const float* k_scale, const float* v_scale, float softmax_scale,
+    int num_partitions, void* out, pa_dtype out_dtype, void* stream);
+
+/*
  * Write-then-attend in one call: the quantize-on-write of the q_len newest
  * tokens of every sequence fused into the decode / verify kernel. The pages
  * write each step's new K/V into the FP8 cache ("1Cat-vLLM 1.0.0" README,

@@ -332,3 +332,29 @@ def test_valid_calls_without_a_device_report_the_launch_error(pa):
         assert _call_decode(pa, q=NUL) == pa.PA_ERR_INVALID_ARG, name
         assert _call_decode(pa, batch=0) == pa.PA_OK, name
         assert pa.pa_last_error() == "", name
+
+
+def _call_noalloc(pa, q_len, **kw):
+    a = _decode_args(**kw)
+    return pa.lib().attn_verify_paged_noalloc(a["q"], a["q_dtype"], a["batch"], q_len, a["kc"],
+                                              a["vc"], a["cache_dtype"], a["bs"], a["nb"],
+                                              a["bt"], a["maxblk"], a["ctx"], a["maxctx"], a["hq"],
+                                              a["hkv"], a["d"], a["ks"], a["vs"], a["scale"],
+                                              a["parts"], a["out"], a["out_dtype"], a["stream"])
+
+
+def test_noalloc_checks_before_launch(pa):
+    assert _call_noalloc(pa, 8, q=NUL) == pa.PA_ERR_INVALID_ARG
+    assert _call_noalloc(pa, 17) == pa.PA_ERR_UNSUPPORTED          # 17 * 4 rows > 64
+    assert _call_noalloc(pa, 8, batch=0) == pa.PA_OK
+    # more partials than the 16 MiB scratch: 64 x 16 x 32 rows x 4096 partitions
+    big = dict(batch=64, hq=32, hkv=8, maxblk=4096, bs=2048, maxctx=1 << 20, parts=64)
+    assert pa.pa_workspace_bytes(pa.PA_OP_VERIFY, 64, 16, 32, 8, 128, 64, 1 << 20) > 16 << 20
+    assert _call_noalloc(pa, 16, **big) == pa.PA_ERR_UNSUPPORTED
+    assert "scratch" in pa.pa_last_error()
+
+
+@pytest.mark.skipif(not _no_device(), reason="launches with fake pointers need a GPU-less host")
+def test_noalloc_without_a_device_reports_the_hip_error(pa):
+    assert _call_noalloc(pa, 8) == pa.PA_ERR_HIP
+    assert pa.pa_last_error() != ""
