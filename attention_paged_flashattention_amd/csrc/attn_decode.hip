@@ -15,8 +15,12 @@
 //   per (sequence, KV head) and shared by the whole group.
 // * S^T = K Q^T with v_mfma_f32_16x16x32 (keys on M, query rows on N). Each
 //   lane loads its key rows straight from HBM with 128-bit loads and
-//   dequantizes them in registers; a tile needs no LDS, because no other wave
-//   reads it. Keys are dealt to MFMA rows so that each lane's S^T outputs are
+//   dequantizes them in registers; no other wave reads a tile. Decode (one
+//   16-row block) keeps two tiles in registers. The verify groups (two or
+//   four row blocks) have registers for one tile only: their loads go from
+//   HBM straight into two wave-private LDS slots (global -> LDS copies, two
+//   tiles ahead) and come back into registers when the tile's turn comes.
+//   Keys are dealt to MFMA rows so that each lane's S^T outputs are
 //   exactly the 16 keys it later feeds as the B operand of O^T += V^T P^T --
 //   P never moves between lanes.
 // * Values are stored dimension-major inside 64-token groups of a page, so a
@@ -87,6 +91,9 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaitVmcnt0 = 0x0F70;
 // Growth of the running max (log2 units) tolerated before O and l are rescaled.
 constexpr float kRescaleSlackD = 8.0f;
+// Cache policy of the global -> LDS copies of the KV stream: non-temporal
+// (the "nt" bit, as the streaming register loads use), read once.
+constexpr int kStreamPolicy = 2;
 
 // Raw cache bytes of one 64-key tile as one lane holds them.
 template <int D, int ES>
@@ -106,6 +113,56 @@ struct TilePages {
 
 __device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// N 16-byte LDS reads at addr + 1024 k (k = 0 .. N-1), and the wait for all
+// of them, in one asm block: the outputs are complete when the block ends.
+template <int N>
+__device__ __forceinline__ void lds_read_tile(u32x4 (&r)[N], uint32_t addr);
+
+template <>
+__device__ __forceinline__ void lds_read_tile<16>(u32x4 (&r)[16], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %16 offset:1024\n"
+      "ds_read_b128 %2, %16 offset:2048\n"
+      "ds_read_b128 %3, %16 offset:3072\n"
+      "ds_read_b128 %4, %16 offset:4096\n"
+      "ds_read_b128 %5, %16 offset:5120\n"
+      "ds_read_b128 %6, %16 offset:6144\n"
+      "ds_read_b128 %7, %16 offset:7168\n"
+      "ds_read_b128 %8, %16 offset:8192\n"
+      "ds_read_b128 %9, %16 offset:9216\n"
+      "ds_read_b128 %10, %16 offset:10240\n"
+      "ds_read_b128 %11, %16 offset:11264\n"
+      "ds_read_b128 %12, %16 offset:12288\n"
+      "ds_read_b128 %13, %16 offset:13312\n"
+      "ds_read_b128 %14, %16 offset:14336\n"
+      "ds_read_b128 %15, %16 offset:15360\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(addr)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_tile<8>(u32x4 (&r)[8], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %8 offset:1024\n"
+      "ds_read_b128 %2, %8 offset:2048\n"
+      "ds_read_b128 %3, %8 offset:3072\n"
+      "ds_read_b128 %4, %8 offset:4096\n"
+      "ds_read_b128 %5, %8 offset:5120\n"
+      "ds_read_b128 %6, %8 offset:6144\n"
+      "ds_read_b128 %7, %8 offset:7168\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(addr)
+      : "memory");
 }
 
 // Fused quantize-on-write: new tokens i0 .. i1-1 of sequence b (positions
@@ -170,6 +227,17 @@ struct DecodePipe {
   static constexpr bool value = FMT != KV_F16 && NQB == 1;
 };
 
+// LDS-staged pipeline for the wider row groups (FP8 cache, two or four 16-row
+// blocks, pages of >= 64 keys so that page ids are scalar loads), whose
+// registers hold one tile but not two: each wave's tiles are
+// copied from HBM straight into two wave-private LDS slots (global -> LDS
+// loads, no registers in flight), two tiles ahead of the one being
+// multiplied, and read back into registers when their turn comes.
+template <int FMT, int NQB, bool UNI>
+struct DecodeLdsPipe {
+  static constexpr bool value = FMT != KV_F16 && NQB >= 2 && UNI;
+};
+
 // APPEND: the fused quantize-on-write of the new tokens. ONEP: a single
 // partition, whose work-group stores the normalised output itself. Both are
 // separate instantiations, so the other kernels carry none of their code.
@@ -184,9 +252,20 @@ void decode_split_kernel(const DecodeArgs a) {
   constexpr int KDW = Tile::KDW, DB = Tile::DB, VDW = Tile::VDW;
   using OpT = typename QOp<QT>::T;
 
-  __shared__ float sm_o[4][D][17];
-  __shared__ float sm_m[4][16];
-  __shared__ float sm_l[4][16];
+  constexpr bool LPIPE = DecodeLdsPipe<FMT, NQB, UNI>::value;
+  // bytes of one wave's tile: 16 bytes per lane per 128-bit load
+  constexpr int TILE_LOADS = 4 * (KDW / 4) + DB * (VDW / 4);
+  constexpr int TILE_BYTES = TILE_LOADS * 1024;
+  // LDS: the two tile slots of each wave (LDS pipeline) and, after the main
+  // loop, the buffers that merge the 4 waves' states (in the slots' space)
+  constexpr int MERGE_FLOATS = 4 * D * 17 + 2 * 4 * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_slots[LPIPE ? 2 * 4 * TILE_BYTES : 1];
+  __shared__ float sm_own[LPIPE ? 1 : MERGE_FLOATS];
+  static_assert(!LPIPE || 2 * 4 * TILE_BYTES >= MERGE_FLOATS * 4, "merge buffers fit");
+  float* sm_base = LPIPE ? reinterpret_cast<float*>(lds_slots) : sm_own;
+  auto sm_o = reinterpret_cast<float (*)[D][17]>(sm_base);
+  auto sm_m = reinterpret_cast<float (*)[16]>(sm_base + 4 * D * 17);
+  auto sm_l = reinterpret_cast<float (*)[16]>(sm_base + 4 * D * 17 + 4 * 16);
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -280,6 +359,70 @@ void decode_split_kernel(const DecodeArgs a) {
       }
   };
 
+  // LDS pipeline: the same 128-bit loads as load(), each one a global -> LDS
+  // copy of 16 bytes per lane (lane i's bytes land at offset 16 i of the
+  // load's 1 KB block of the slot), and the read-back that gives every lane
+  // exactly the words load() would have given it.
+  // Copies for a tile j >= J (issued only to keep the number of loads per
+  // iteration fixed) all read the first 16 bytes of the group's first query
+  // row, which this wave has just loaded (a cache hit, no HBM traffic); the
+  // slot they fill is never read.
+  [[maybe_unused]] const uint8_t* dummy = reinterpret_cast<const uint8_t*>(
+      a.q + ((int64_t)b * a.q_len * a.num_q_heads + (int64_t)g * G) * D);
+  [[maybe_unused]] auto dma = [&](uint8_t* slot, int j, const TilePages& pg) {
+    const bool real = j < J;
+    const int t0 = tile_t0(j);
+    const int tk = t0 + 16 * (c >> 2);
+    const int tv = t0 + 16 * qg;
+    const uint8_t* kp = a.key_cache +
+        (((pg.k * kv_heads + g) << bs_log2) + (tk & bs_mask) + (c & 3)) * (int64_t)(D * ES) +
+        RUN * qg * ES;
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int x = 0; x < KDW / 4; ++x, ++n)
+        __builtin_amdgcn_global_load_lds(real ? kp + (int64_t)4 * s * D * ES + 16 * x : dummy,
+                                         slot + n * 1024, 16, 0, kStreamPolicy);
+    const int vo = tv & bs_mask;
+    const uint8_t* vp = a.value_cache +
+        (((((pg.v * kv_heads + g) << (bs_log2 - vg_log2)) + (vo >> vg_log2)) * D + c) << vg_log2 |
+         (vo & ((1 << vg_log2) - 1))) * (int64_t)ES;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int x = 0; x < VDW / 4; ++x, ++n)
+        __builtin_amdgcn_global_load_lds(
+            real ? vp + ((int64_t)(db * 16) << vg_log2) * ES + 16 * x : dummy, slot + n * 1024,
+            16, 0, kStreamPolicy);
+  };
+  // The read-back is one asm block that ends with its own wait for the
+  // reads: the compiler cannot tell which slot a pending global -> LDS copy
+  // writes, and before reads it can see it waits for every copy in flight
+  // (the next tiles' too), which would drain the pipeline each tile. The
+  // explicit waits in the main loop order the copies before these reads.
+  [[maybe_unused]] auto unstage = [&](Tile& T, const uint8_t* slot) {
+    u32x4 r[TILE_LOADS];
+    const uint32_t addr =
+        (uint32_t)reinterpret_cast<uintptr_t>(slot) + (uint32_t)lane * 16u;
+    lds_read_tile<TILE_LOADS>(r, addr);
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int x = 0; x < KDW / 4; ++x, ++n) {
+        T.k[s][4 * x] = r[n].x; T.k[s][4 * x + 1] = r[n].y;
+        T.k[s][4 * x + 2] = r[n].z; T.k[s][4 * x + 3] = r[n].w;
+      }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int x = 0; x < VDW / 4; ++x, ++n) {
+        T.v[db][4 * x] = r[n].x; T.v[db][4 * x + 1] = r[n].y;
+        T.v[db][4 * x + 2] = r[n].z; T.v[db][4 * x + 3] = r[n].w;
+      }
+  };
+
   const float C =
       a.softmax_scale * (a.k_scale ? ld_const(a.k_scale, g) : 1.0f) * kv_fold<FMT>() * kLog2e;
 
@@ -304,7 +447,12 @@ void decode_split_kernel(const DecodeArgs a) {
   const bool pre = UNI && !win;
   if (J > 0) P0 = pre ? TilePages{pre0, pre0} : pages(0);
   if (J > 1) P1 = pre ? TilePages{pre1, pre1} : pages(1);
-  if (J > 0) load(A, 0, P0);
+  [[maybe_unused]] uint8_t* slot_a = lds_slots + (LPIPE ? w * TILE_BYTES : 0);
+  [[maybe_unused]] uint8_t* slot_b = lds_slots + (LPIPE ? (4 + w) * TILE_BYTES : 0);
+  [[maybe_unused]] TilePages P2{0, 0};
+  if constexpr (!LPIPE) {
+    if (J > 0) load(A, 0, P0);
+  }
   (void)B;
 
   // Query operands (B of S^T = K Q^T): row r = nb*16 + c, head dims
@@ -321,6 +469,18 @@ void decode_split_kernel(const DecodeArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) qop[nb][j] = OpT{};
+    }
+  }
+
+  if constexpr (LPIPE) {
+    // tiles 0 and 1 into the wave's two slots (tile 1 a dummy copy when
+    // J = 1: the same number of loads whatever J is), with tile 2's page ids
+    // between them as in the loop below. Issued after the query loads, so
+    // that waiting for those never waits for the tiles.
+    if (J > 0) {
+      dma(slot_a, 0, P0);
+      P2 = pages(min(2, J - 1));
+      dma(slot_b, 1, J > 1 ? P1 : P0);
     }
   }
 
@@ -462,6 +622,36 @@ void decode_split_kernel(const DecodeArgs a) {
     } else if (j < J) {
       compute(A, j);
     }
+  } else if constexpr (LPIPE) {
+    // Tile j sits in slot j % 2; once it is back in registers the slot takes
+    // tile j + 2 (past the last tile, a cache-hit copy that is never read:
+    // every iteration issues the same loads), so two tiles stream in while
+    // one is multiplied. The compiler does not order the global -> LDS
+    // copies before the reads of their slot, so each read is preceded by an
+    // explicit wait: issued after tile j's copies are exactly the next
+    // tile's copies (page ids are scalar loads), so waiting until that many
+    // vector-memory operations remain means tile j has landed.
+    constexpr int kAfter = TILE_LOADS;
+    constexpr int kWaitTile = (kAfter & 15) | ((kAfter >> 4) << 14) | 0x0F70;
+    static_assert(kAfter < 64, "vmcnt holds 6 bits");
+    if (J > 0) {
+      for (int j = 0; j < J; j += 2) {
+        __builtin_amdgcn_s_waitcnt(kWaitTile);
+        unstage(A, slot_a);                         // (ends with its reads done)
+        P0 = pages(min(j + 3, J - 1));
+        dma(slot_a, j + 2, P2);
+        compute(A, j);
+        if (j + 1 >= J) break;
+        __builtin_amdgcn_s_waitcnt(kWaitTile);
+        unstage(A, slot_b);
+        P2 = pages(min(j + 4, J - 1));
+        dma(slot_b, j + 3, P0);
+        compute(A, j + 1);
+      }
+    }
+    // every copy into the slots has landed before they become merge buffers
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
   } else {
     // One stage; page ids one tile ahead.
     for (int j = 0; j < J; ++j) {
