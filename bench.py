@@ -33,6 +33,7 @@ already resident in HBM when a timed region starts.
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -47,7 +48,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS_16 = 2500.0    # MI355X dense fp16 / bf16 MFMA
 METRIC = "paged-attn decode GB/s (%HBM peak) @128K FP8 KV; prefill TFLOP/s @32K"
 SECTIONS = ["decode128k", "prefill32k", "verify128k", "verify_q16", "decode256k", "decode_b8",
-            "decode_b16", "window", "prefill64k", "small", "empty", "copy"]
+            "decode_b16", "window", "prefill64k", "prefill128k", "prefill256k", "small", "empty",
+            "copy"]
 
 
 def log(msg):
@@ -456,63 +458,104 @@ def copy_section(ev, steps):
     return dict(bytes=2 * nbytes, ms=ms, GBps=2 * nbytes / ms / 1e6)
 
 
-def cpu_baseline(seconds_target=10.0):
-    """The oracle, as it stands, on a bounded sample of the 128K decode step:
-    2 of the 8 KV heads (8 of 32 query heads) over the full context. The
-    oracle's cache for those heads is built untimed (the cache is resident on
-    the GPU side too); timed: the oracle's write of the newest token and its
-    attention for the 8 sampled query heads, repeated to ~10 s."""
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        return _cpu_baseline(seconds_target)
-
-
-def _cpu_baseline(seconds_target):
+def cpu_baseline(gpu_ms):
+    """The oracle, as it stands, timed on the host's cores for every workload
+    (tests/oracle_pool.py: the work is split by (sequence, KV head) over worker
+    processes with one BLAS thread each; oracle/ itself is unchanged). The
+    oracle's paged cache is built first, untimed (on the GPU side the cache is
+    resident too); timed is one step of the workload: the write of the newest
+    tokens and the attention of every row (for the 32K prefill: the last 4096-
+    token chunk, every row, which is also its heaviest). ``value`` is the 128K
+    decode step in GB/s of algorithmic bytes, the unit of the headline.
+    ``gpu_ms`` maps workload names to the GPU's step time for the same step."""
+    import numpy as np
     from attention_paged_flashattention_amd import synth
-    from oracle import attention, paged
+    from tests.oracle_pool import OraclePool, default_workers, row_tasks
 
-    case = synth.headline_decode_128k()
-    heads_kv = [0, 5]
-    fill = synth.POISON["e4m3"]
-    kc, vc = paged.new_caches(case.num_blocks, case.num_kv_heads, case.block_size,
-                              case.head_dim, "e4m3", fill=fill)
-    ctx = int(case.ctx_lens[0])
-    slots = case.slot_mapping
-    bs = case.block_size
-    T = paged.value_group(bs)
-    k32 = synth.to_f32(case.k, "f16")
-    v32 = synth.to_f32(case.v, "f16")
-    for g in heads_kv:
-        page, off = slots[:ctx - 1] // bs, slots[:ctx - 1] % bs
-        kc[page, g, off, :] = paged.quantize(k32[:ctx - 1, g, :], "e4m3", case.k_scale[g])
-        vc[page, g, off // T, :, off % T] = paged.quantize(v32[:ctx - 1, g, :], "e4m3",
-                                                           case.v_scale[g])
-    q32 = synth.to_f32(case.q, "f16")
-    G = case.gqa
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for g in heads_kv:
-            t = ctx - 1
-            page, off = slots[t] // bs, slots[t] % bs
-            kc[page, g, off, :] = paged.quantize(k32[t, g, :], "e4m3", case.k_scale[g])
-            vc[page, g, off // T, :, off % T] = paged.quantize(v32[t, g, :], "e4m3",
-                                                               case.v_scale[g])
-            heads = [g * G + i for i in range(G)]
-            attention.attend_rows(q32[0, heads], heads, [ctx - 1] * G, ctx, kc, vc,
-                                  case.block_tables[0], "e4m3", case.num_q_heads,
-                                  case.num_kv_heads, case.softmax_scale, case.k_scale,
-                                  case.v_scale)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds_target:
-            break
-    dt = time.perf_counter() - t0
-    sample_bytes = len(heads_kv) * ctx * case.head_dim * 2 * reps
-    return dict(value=sample_bytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=(f"2 of 8 KV heads (8 of 32 query heads) of the 128K E4M3 decode step, "
-                        f"full 131072-token context, {reps} repetitions in {dt:.1f} s; numpy "
-                        f"float64, BLAS limited to 1 thread; host has {os.cpu_count()} CPUs"),
-                seconds=dt)
+    workers = default_workers()
+    per = {}
+
+    def decode_step(case, name, q_len, unit_bytes):
+        pairs = [(b, g) for b in range(case.batch) for g in range(case.num_kv_heads)]
+        with OraclePool(case, workers=workers) as pool:
+            t0 = time.perf_counter()
+            # every token but the newest q_len of each sequence: setup
+            tasks = []
+            for b, g in pairs:
+                c = int(case.ctx_lens[b])
+                step = max(1, -(-(c - q_len) // max(1, 32 // len(pairs))))
+                for lo in range(0, c - q_len, step):
+                    tasks.append({"write": [dict(b=b, g=g, t_lo=lo, t_hi=min(c - q_len, lo + step))]})
+            pool.run(tasks)
+            setup = time.perf_counter() - t0
+            tasks = []
+            for b, g in pairs:
+                c = int(case.ctx_lens[b])
+                t, _ = row_tasks(case, b, g, np.arange(q_len))
+                t[0]["write"] = [dict(b=b, g=g, t_lo=c - q_len, t_hi=c)]
+                tasks += t
+            pool.run(tasks)
+            wall = pool.last_wall
+        kv = sum(int(x) for x in case.ctx_lens) * case.num_kv_heads * case.head_dim * 2
+        per[name] = dict(oracle_s=round(wall, 3), setup_s=round(setup, 1), unit=unit_bytes,
+                         oracle_GBps=round(kv / wall / 1e9, 4),
+                         gpu_ms=None if gpu_ms.get(name) is None else round(gpu_ms[name], 4))
+        if gpu_ms.get(name):
+            per[name]["gpu_over_oracle"] = round(wall * 1e3 / gpu_ms[name], 1)
+        log(f"cpu baseline {name}: {wall:.2f} s on {workers} workers")
+
+    decode_step(synth.headline_decode_128k(), "decode_128k_e4m3_bs2048_p32", 1, "step")
+    decode_step(synth.batched_decode_e4m3(), "decode_b8_1k4k_e4m3_bs16", 1, "step")
+    decode_step(synth.verify_q8_128k(), "verify_q8_b4_128k_e5m2_bs2048", 8, "step")
+    decode_step(synth.long_decode_256k(), "decode_256k_e4m3_bs2048_p64", 1, "step")
+
+    # workload 1: the 64-token prefill and the decode at 64, every row (tiny)
+    small = synth.prefill_decode_small()
+    with OraclePool(small, workers=1) as pool:
+        pool.build([(0, 0)], token_range=(0, 64))
+        t, _ = row_tasks(small, 0, 0, np.arange(64), keys=64)
+        pool.run(t)
+        w_pf = pool.last_wall
+        t, _ = row_tasks(small, 0, 0, np.arange(64, 65))
+        t[0]["write"] = [dict(b=0, g=0, t_lo=64, t_hi=65)]
+        pool.run(t)
+        w_dec = pool.last_wall
+    per["prefill64_decode_fp16_d64"] = dict(oracle_s=round(w_pf + w_dec, 4), unit="prefill 64 + decode")
+
+    # the 32K prefill: the last chunk (ctx 32768), write + every row
+    case = synth.chunked_prefill_32k()
+    chunk = case.meta["chunk"]
+    with OraclePool(case, workers=workers) as pool:
+        t0 = time.perf_counter()
+        pool.build([(0, g) for g in range(case.num_kv_heads)], token_range=(0, 32768 - chunk),
+                   pieces=4)
+        setup = time.perf_counter() - t0
+        tasks = []
+        for g in range(case.num_kv_heads):
+            t, _ = row_tasks(case, 0, g, np.arange(32768 - chunk, 32768), split=8)
+            t[0]["write"] = [dict(b=0, g=g, t_lo=32768 - chunk, t_hi=32768)]
+            tasks += t
+        pool.run(tasks)
+        wall = pool.last_wall
+    flops = 4 * 128 * 32 * (chunk * (32768 - chunk) + chunk * (chunk + 1) // 2)
+    per["prefill32k_chunk4k_bf16_e4m3_bs2048"] = dict(
+        oracle_s=round(wall, 2), setup_s=round(setup, 1), unit="last 4096-token chunk",
+        oracle_TFLOPs=round(flops / wall / 1e12, 5),
+        gpu_ms=None if gpu_ms.get("prefill32k_last_chunk") is None
+        else round(gpu_ms["prefill32k_last_chunk"], 4))
+    if gpu_ms.get("prefill32k_last_chunk"):
+        per["prefill32k_chunk4k_bf16_e4m3_bs2048"]["gpu_over_oracle"] = round(
+            wall * 1e3 / gpu_ms["prefill32k_last_chunk"], 1)
+    log(f"cpu baseline prefill 32K last chunk: {wall:.2f} s")
+
+    h = per["decode_128k_e4m3_bs2048_p32"]
+    return dict(value=h["oracle_GBps"], unit="GB/s", cores=os.cpu_count(), workers=workers,
+                kind="oracle",
+                sample=("every workload at full size, one step each (the 32K prefill: its last "
+                        "4096-token chunk); the oracle's cache built untimed; numpy float64 in "
+                        f"{workers} worker processes with one BLAS thread each, split by "
+                        "(sequence, KV head); value = the 128K E4M3 decode step"),
+                per_config=per)
 
 
 def main():
@@ -600,6 +643,15 @@ def main():
             log(f"section prefill64k chunk {chunk}")
             res[f"prefill64k_{chunk}"] = prefill_section(ev, synth.chunked_prefill_64k(chunk=chunk),
                                                          max(5, K // 10), 1)
+    for tot, sec in ((131072, "prefill128k"), (262144, "prefill256k")):
+        if sec in sections:
+            base = synth.chunked_prefill_long(tot, 4096)
+            for chunk in (4096, 8192):
+                log(f"section {sec} chunk {chunk}")
+                case = dataclasses.replace(base, meta=dict(base.meta, chunk=chunk),
+                                           name=base.name.replace("chunk4k", f"chunk{chunk // 1024}k"))
+                res[f"{sec}_{chunk}"] = prefill_section(ev, case, 3 if tot == 131072 else 2, 1)
+            del base
     if "small" in sections:
         log("section small")
         res["small"] = small_section(ev, K)
@@ -610,7 +662,16 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and "decode128k" in sections:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline()
+        gpu_ms = {}
+        for key, name in (("decode128k", "decode_128k_e4m3_bs2048_p32"),
+                          ("decode_b8_fused", "decode_b8_1k4k_e4m3_bs16"),
+                          ("verify128k_fused", "verify_q8_b4_128k_e5m2_bs2048"),
+                          ("decode256k", "decode_256k_e4m3_bs2048_p64")):
+            if key in res:
+                gpu_ms[name] = res[key]["ms_per_step"]
+        if "prefill32k" in res:
+            gpu_ms["prefill32k_last_chunk"] = res["prefill32k"]["last_chunk_ms"]
+        cpu = cpu_baseline(gpu_ms)
 
     dec_sha = source_hash("attn_decode.hip", "pa_device.h")
     pf_sha = source_hash("attn_prefill.hip", "pa_device.h")
@@ -704,16 +765,17 @@ def main():
                 "split_kernel_us": round(r["split_ms"] * 1e3, 2),
                 "split_kernel_GBps": round(r["split_GBps"], 1),
                 "bytes_in_window_per_step": r["step_bytes"]}
-    for chunk in (4096, 8192):
-        r = res.get(f"prefill64k_{chunk}")
-        if r:
-            line[f"prefill_64k_chunk{chunk // 1024}k"] = {
-                "workload": r["name"], "TFLOPs": round(r["TFLOPs"], 1),
-                "ms_per_step": round(r["ms_per_step"], 3),
-                "frac_of_peak": round(r["TFLOPs"] / MFMA_PEAK_TFLOPS_16, 4),
-                "kernel_TFLOPs": round(r["kernel_TFLOPs"], 1),
-                "last_chunk_TFLOPs": round(r["last_chunk_TFLOPs"], 1),
-                "launches_per_step": r["launches_per_step"]}
+    for sec, tag in (("prefill64k", "64k"), ("prefill128k", "128k"), ("prefill256k", "256k")):
+        for chunk in (4096, 8192):
+            r = res.get(f"{sec}_{chunk}")
+            if r:
+                line[f"prefill_{tag}_chunk{chunk // 1024}k"] = {
+                    "workload": r["name"], "TFLOPs": round(r["TFLOPs"], 1),
+                    "ms_per_step": round(r["ms_per_step"], 3),
+                    "frac_of_peak": round(r["TFLOPs"] / MFMA_PEAK_TFLOPS_16, 4),
+                    "kernel_TFLOPs": round(r["kernel_TFLOPs"], 1),
+                    "last_chunk_TFLOPs": round(r["last_chunk_TFLOPs"], 1),
+                    "launches_per_step": r["launches_per_step"]}
     if "small" in res:
         line["small_prefill64_decode_latency"] = dict(res["small"], workload="prefill64_decode_fp16_d64")
     if "empty" in res:
