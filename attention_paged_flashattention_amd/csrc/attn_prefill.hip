@@ -419,14 +419,15 @@ void prefill_kernel(const PrefillArgs a) {
       qk(n % NBUF);
     }
     __syncthreads();
-    // phase 2
-    if (n + 2 < ntiles) store_kv(Rs, (n + 2) % NBUF, (n + 2) * BN);
+    // phase 2 (tile n+2 is staged after each group's own work: the matrix
+    // group's conversions then overlap its last MFMAs)
     if (!grp_b) {
       pv(n % NBUF);
       if (n + 1 < ntiles) qk((n + 1) % NBUF);
     } else {
       softmax(n * BN);
     }
+    if (n + 2 < ntiles) store_kv(Rs, (n + 2) % NBUF, (n + 2) * BN);
     __syncthreads();
   };
   // pairs of tiles, so the loop body always issues the same loads
