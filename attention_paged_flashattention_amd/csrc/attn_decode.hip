@@ -316,9 +316,14 @@ void decode_split_kernel(const DecodeArgs a) {
     if constexpr (UNI) {
       pg.k = pg.v = ld_const(btb, t0 >> bs_log2);
     } else {
+      // Both entries are loaded whatever the context length (indices clamped
+      // to the block-table row), so the loads need not wait for it; a run
+      // past the context takes page 0 instead of the entry it read.
       const int tk = t0 + 16 * (c >> 2), tv = t0 + 16 * qg;
-      pg.k = tk < ctx ? btb[tk >> bs_log2] : 0;
-      pg.v = tv < ctx ? btb[tv >> bs_log2] : 0;
+      const int32_t rk = btb[min(tk >> bs_log2, a.max_blocks - 1)];
+      const int32_t rv = btb[min(tv >> bs_log2, a.max_blocks - 1)];
+      pg.k = tk < ctx ? rk : 0;
+      pg.v = tv < ctx ? rv : 0;
     }
     return pg;
   };
