@@ -195,6 +195,29 @@ def test_verify_parity(runner, fmt, B, ctx, q_len, Hq, Hkv, D, bs, parts):
     check_close(out, ref, fmt, "verify f32")
 
 
+# the verify groups' LDS pipeline (pages of >= 64 keys, 32-64 rows): partitions shorter than
+# the 4 waves' share of tiles, empty partitions, a ragged last tile, bf16 queries
+LDS_VERIFY_CASES = [
+    # fmt, B, ctx, q_len, bs, parts, q_dtype
+    ("e5m2", 2, (16, 3000), 16, 64, 4, "f16"),
+    ("e4m3", 3, (8, 70, 1500), 8, 64, 8, "f16"),
+    ("e4m3", 2, (300, 2000), 12, 128, 0, "bf16"),
+    ("e5m2", 1, (4100,), 16, 2048, 3, "bf16"),
+]
+
+
+@pytest.mark.parametrize("fmt,B,ctx,q_len,bs,parts,q_dtype", LDS_VERIFY_CASES)
+def test_verify_parity_lds_pipeline(runner, fmt, B, ctx, q_len, bs, parts, q_dtype):
+    log(f"verify (LDS pipeline) {fmt} B={B} ctx={ctx} q_len={q_len} bs={bs} P={parts} q={q_dtype}")
+    case = _mk(fmt, B, ctx, q_len, 32, 8, 128, bs, q_dtype, sigma_kv=0.5)
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.verify(q_len, num_partitions=parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle_full(case).reshape(B, q_len, 32, 128)
+    check_close(out, ref, fmt, "verify f32")
+
+
 def test_verify_rows_equal_decodes(runner):
     """The grouped verifier is exact: row i equals a decode at ctx - q_len + 1 + i
     (same kernels, so compared within fp32 rounding of the partition merge)."""
