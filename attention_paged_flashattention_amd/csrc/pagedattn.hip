@@ -220,6 +220,8 @@ pa_status decode_like(const char* name, const void* q, pa_dtype q_dtype, int bat
                 name, q_len * G, kMaxRows);
   if (num_partitions > kMaxParts)
     return fail(PA_ERR_UNSUPPORTED, "%s: at most %d partitions", name, kMaxParts);
+  if (batch > 65535)   // a grid dimension
+    return fail(PA_ERR_UNSUPPORTED, "%s: at most 65535 sequences per call", name);
   if (k_new && (int64_t)batch * q_len * hkv * (head_dim / 4) > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "%s: too many new tokens for one call", name);
   if (batch == 0) return ok();

@@ -165,6 +165,8 @@ PA_API pa_status attn_prefill_paged(
  * merges them by log-sum-exp in a fixed order.
  *
  *   q              [batch][num_q_heads][head_dim], F16 or BF16
+ *   batch          at most 65535 (PA_ERR_UNSUPPORTED above: a launch dimension;
+ *                  the same holds for the verify, window and append calls)
  *   num_partitions 0 = automatic (pa_decode_partitions), else >= 1
  *   workspace      device scratch of at least pa_workspace_bytes(PA_OP_DECODE,
  *                  ...) bytes, 256-byte aligned; contents need no

@@ -109,6 +109,7 @@ def _call_verify(pa, q_len, **kw):
     (dict(wsb=16), 1),
     (dict(ws=ctypes.c_void_p(0x1010)), 1),   # misaligned workspace
     (dict(hq=128, hkv=1), 2),                # G = 128 rows exceed one decode group
+    (dict(batch=65536), 2),                  # a launch dimension
 ])
 def test_decode_rejects_before_launch(pa, kw, status):
     assert _call_decode(pa, **kw) == status
