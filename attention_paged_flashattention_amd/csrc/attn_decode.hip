@@ -115,6 +115,18 @@ __device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Raw buffer descriptor over one page's bytes (base: wave-uniform; no stride;
+// range checking left wide open: every offset used lies inside the page).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
+// 16 bytes at byte offset off of the buffer, non-temporal like ld16_stream.
+__device__ __forceinline__ u32x4 ld16_buf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy));
+}
+
 // N 16-byte LDS reads at addr + 1024 k (k = 0 .. N-1), and the wait for all
 // of them, in one asm block: the outputs are complete when the block ends.
 template <int N>
@@ -334,10 +346,44 @@ void decode_split_kernel(const DecodeArgs a) {
   // select -- S to -inf, V to zero -- whatever the stale slot holds. Keeping
   // the loads unconditional lets the compiler count them exactly, so one
   // tile's loads stay in flight while another is multiplied.
+  //
+  // With pages of >= 64 keys the tile lies in one page: its K rows and its
+  // value group are addressed from the page's base (a scalar, one buffer
+  // descriptor per tile) plus per-lane 32-bit offsets fixed for the whole
+  // loop. Buffer loads need no per-lane 64-bit address arithmetic, and the
+  // 128K decode measured 2-4% faster with them than with global loads of the
+  // same addresses and the same non-temporal hint.
   auto load = [&](Tile& T, int j, const TilePages& pg) {
     const int t0 = tile_t0(j);
     const int tk = t0 + 16 * (c >> 2);  // first key of this lane's K run
     const int tv = t0 + 16 * qg;        // first key of this lane's V run
+    if constexpr (UNI) {
+      const uint8_t* kb = a.key_cache + ((pg.k * kv_heads + g) << bs_log2) * (int64_t)(D * ES);
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb);
+      const int ko = (((tk & bs_mask) + (c & 3)) * D + RUN * qg) * ES;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int x = 0; x < KDW / 4; ++x) {
+          u32x4 v = ld16_buf(kr, ko + 4 * s * D * ES + 16 * x);
+          T.k[s][4 * x] = v.x; T.k[s][4 * x + 1] = v.y;
+          T.k[s][4 * x + 2] = v.z; T.k[s][4 * x + 3] = v.w;
+        }
+      // the tile's 64-token value group: [D][64] elements
+      const uint8_t* vb = a.value_cache +
+          ((((pg.v * kv_heads + g) << (bs_log2 - 6)) + ((t0 & bs_mask) >> 6)) * D << 6) * (int64_t)ES;
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb);
+      const int vo = ((c << 6) | (16 * qg)) * ES;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int x = 0; x < VDW / 4; ++x) {
+          u32x4 v = ld16_buf(vr, vo + ((db * 16) << 6) * ES + 16 * x);
+          T.v[db][4 * x] = v.x; T.v[db][4 * x + 1] = v.y;
+          T.v[db][4 * x + 2] = v.z; T.v[db][4 * x + 3] = v.w;
+        }
+      return;
+    }
     const uint8_t* kp = a.key_cache +
         (((pg.k * kv_heads + g) << bs_log2) + (tk & bs_mask) + (c & 3)) * (int64_t)(D * ES) +
         RUN * qg * ES;
