@@ -421,32 +421,35 @@ void decode_split_kernel(const DecodeArgs a) {
   [[maybe_unused]] const uint8_t* dummy = reinterpret_cast<const uint8_t*>(
       a.q + ((int64_t)b * a.q_len * a.num_q_heads + (int64_t)g * G) * D);
   [[maybe_unused]] auto dma = [&](uint8_t* slot, int j, const TilePages& pg) {
+    // buffer copies from the page base (the LDS pipeline runs with pages of
+    // >= 64 keys only), as in load(); a dummy copy reads offset 0 of a
+    // descriptor over the query row
     const bool real = j < J;
     const int t0 = tile_t0(j);
-    const int tk = t0 + 16 * (c >> 2);
-    const int tv = t0 + 16 * qg;
-    const uint8_t* kp = a.key_cache +
-        (((pg.k * kv_heads + g) << bs_log2) + (tk & bs_mask) + (c & 3)) * (int64_t)(D * ES) +
-        RUN * qg * ES;
+    const uint8_t* kb = a.key_cache + ((pg.k * kv_heads + g) << bs_log2) * (int64_t)(D * ES);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(real ? kb : dummy);
+    const int ko = real ? ((((t0 + 16 * (c >> 2)) & bs_mask) + (c & 3)) * D + RUN * qg) * ES : 0;
     int n = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int x = 0; x < KDW / 4; ++x, ++n)
-        __builtin_amdgcn_global_load_lds(real ? kp + (int64_t)4 * s * D * ES + 16 * x : dummy,
-                                         slot + n * 1024, 16, 0, kStreamPolicy);
-    const int vo = tv & bs_mask;
-    const uint8_t* vp = a.value_cache +
-        (((((pg.v * kv_heads + g) << (bs_log2 - vg_log2)) + (vo >> vg_log2)) * D + c) << vg_log2 |
-         (vo & ((1 << vg_log2) - 1))) * (int64_t)ES;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void*)(slot + n * 1024), 16,
+            real ? ko + 4 * s * D * ES + 16 * x : 0, 0, 0, kStreamPolicy);
+    const uint8_t* vb = a.value_cache +
+        ((((pg.v * kv_heads + g) << (bs_log2 - 6)) + ((t0 & bs_mask) >> 6)) * D << 6) * (int64_t)ES;
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(real ? vb : dummy);
+    const int vo = real ? ((c << 6) | (16 * qg)) * ES : 0;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int x = 0; x < VDW / 4; ++x, ++n)
-        __builtin_amdgcn_global_load_lds(
-            real ? vp + ((int64_t)(db * 16) << vg_log2) * ES + 16 * x : dummy, slot + n * 1024,
-            16, 0, kStreamPolicy);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void*)(slot + n * 1024), 16,
+            real ? vo + ((db * 16) << 6) * ES + 16 * x : 0, 0, 0, kStreamPolicy);
   };
+
   // The read-back is one asm block that ends with its own wait for the
   // reads: the compiler cannot tell which slot a pending global -> LDS copy
   // writes, and before reads it can see it waits for every copy in flight
