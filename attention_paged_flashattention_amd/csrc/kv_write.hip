@@ -27,12 +27,13 @@ namespace pa {
 // 4 source elements (8 bytes) -> 4 FP8 codes.
 template <int ST, int FMT>
 __device__ __forceinline__ uint32_t encode4(u32x2 w, bool scaled, const Divisor& div) {
-  float y[4];
+  float x[4], y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x = src_to_f32<ST>((uint16_t)((i < 2 ? w.x : w.y) >> ((i & 1) * 16)));
-    y[i] = scaled ? div_rn(x, div) : x;   // x / scale, correctly rounded
+    x[i] = src_to_f32<ST>((uint16_t)((i < 2 ? w.x : w.y) >> ((i & 1) * 16)));
+    y[i] = x[i];
   }
+  if (scaled) divide_n<4>(y, x, div);   // x / scale, correctly rounded
   return fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]);
 }
 

@@ -134,6 +134,25 @@ __device__ __forceinline__ float src_to_f32(uint16_t bits) {
   }
 }
 
+// y[i] = x[i] / s, correctly rounded, for N elements: the three-operation
+// quotient for all of them, and the division itself only in the (rare) lanes
+// where some element lies outside the shortcut's range -- one branch per N
+// elements instead of one per element.
+template <int N>
+__device__ __forceinline__ void divide_n(float (&y)[N], const float (&x)[N], const Divisor& d) {
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    y[i] = div_fast(x[i], d);
+    ok = ok & div_fast_ok(x[i], d);
+  }
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!div_fast_ok(x[i], d)) y[i] = x[i] / d.s;
+  }
+}
+
 // 8 source elements (one 16-byte chunk) -> 8 cache codes: FP8 in the low 8
 // bytes, or the fp16 elements unchanged.
 template <int ST, int FMT>
@@ -142,12 +161,13 @@ __device__ __forceinline__ u32x4 encode8(u32x4 w, bool scaled, const Divisor& di
     return w;
   } else {
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float y[8];
+    float x[8], y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = src_to_f32<ST>((uint16_t)(ww[i >> 1] >> ((i & 1) * 16)));
-      y[i] = scaled ? div_rn(x, div) : x;   // x / scale, correctly rounded
+      x[i] = src_to_f32<ST>((uint16_t)(ww[i >> 1] >> ((i & 1) * 16)));
+      y[i] = x[i];
     }
+    if (scaled) divide_n<8>(y, x, div);   // x / scale, correctly rounded
     return u32x4{fp8x4_from_f32<FMT>(y[0], y[1], y[2], y[3]),
                  fp8x4_from_f32<FMT>(y[4], y[5], y[6], y[7]), 0u, 0u};
   }

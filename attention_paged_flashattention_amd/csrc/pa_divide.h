@@ -8,13 +8,13 @@
 
 namespace pa {
 
-// A divisor s with r = 1/s correctly rounded. `fast` holds when s and r are
-// both normal floats: then x / s can be formed from r (below); otherwise
-// (zero, subnormal, infinite or NaN s, or a reciprocal that is subnormal or
-// overflows) every quotient is a plain division.
+// A divisor s with r = 1/s correctly rounded, and the range [lo, hi] of |x|
+// over which x / s can be formed from r (below). The range is empty unless s
+// and r are both normal floats (otherwise -- zero, subnormal, infinite or NaN
+// s, or a reciprocal that is subnormal or overflows -- every quotient is a
+// plain division).
 struct Divisor {
-  float s, r;
-  bool fast;
+  float s, r, lo, hi;
 };
 
 __host__ __device__ inline bool is_normal_finite(float v) {
@@ -22,36 +22,49 @@ __host__ __device__ inline bool is_normal_finite(float v) {
   return a >= 0x1p-126f && a <= 3.40282347e38f;
 }
 
+// The shortcut below is exact when |x| >= 2^-100 and 2^-100 <= |x r| <= 2^100
+// (Markstein's conditions, see div_fast). lo and hi bound |x| so that both
+// hold with a factor of two to spare, whatever the rounding of lo, hi and x r:
+// |x| >= lo gives |x r| >= 2^-99 (1 - 2^-24)^2 > 2^-100, and |x| <= hi gives
+// |x r| <= 2^99 (1 + 2^-24)^2 < 2^100. hi is finite, so x = inf falls outside.
 __host__ __device__ inline Divisor make_divisor(float s) {
   Divisor d;
   d.s = s;
   d.r = 1.0f / s;
-  d.fast = is_normal_finite(s) && is_normal_finite(d.r);
+  if (is_normal_finite(s) && is_normal_finite(d.r)) {
+    const float ar = __builtin_fabsf(d.r);
+    d.lo = __builtin_fmaxf(0x1p-100f, 0x1p-99f / ar);
+    d.hi = __builtin_fminf(0x1p99f / ar, 3.40282347e38f);
+  } else {
+    d.lo = __builtin_inff();
+    d.hi = 0.0f;
+  }
   return d;
 }
 
+// Whether div_fast(x, d) is the correctly rounded x / s (false for zeros,
+// NaN, infinities, and |x| outside [lo, hi]).
+__host__ __device__ inline bool div_fast_ok(float x, const Divisor& d) {
+  const float ax = __builtin_fabsf(x);
+  return ax >= d.lo && ax <= d.hi;
+}
+
+// x / s from r: q = x * r is within an ulp of x / s, the remainder x - s * q
+// is exact under fma, and one correction q + r * (x - s q), rounded once, is
+// the correctly rounded quotient (Markstein's theorem for round-to-nearest;
+// an exact q has a zero remainder and comes back unchanged). Three operations;
+// valid where div_fast_ok holds.
+__host__ __device__ inline float div_fast(float x, const Divisor& d) {
+  const float q = x * d.r;
+  const float e = __builtin_fmaf(-q, d.s, x);
+  return __builtin_fmaf(e, d.r, q);
+}
+
 // x / s, correctly rounded (round to nearest even), equal bit for bit to IEEE
-// float32 division. From r: q = x * r is within an ulp of x / s, the
-// remainder x - s * q is exact under fma, and one correction q + r * (x - s q)
-// rounded once is the correctly rounded quotient (Markstein's theorem for
-// round-to-nearest). The theorem needs every step clear of underflow and
-// overflow, which holds when s and r are normal, |x| >= 2^-100 and
-// 2^-100 <= |q| <= 2^100 (the remainder is then a multiple of at least
-// 2^-150 of 24 significant bits, and nothing overflows). An exact q (zero
-// remainder) is returned as it is. Everything else -- zeros, tiny or huge
-// quotients, infinities, NaN, a divisor outside the fast range -- takes the
-// division itself (the build makes it correctly rounded). Three operations
-// per element on the fast path.
+// float32 division: the shortcut where it is exact, the division itself (the
+// build makes it correctly rounded) everywhere else.
 __host__ __device__ inline float div_rn(float x, const Divisor& d) {
-  if (d.fast) {
-    const float q = x * d.r;
-    const float aq = __builtin_fabsf(q);
-    if (aq >= 0x1p-100f && aq <= 0x1p100f && __builtin_fabsf(x) >= 0x1p-100f) {
-      const float e = __builtin_fmaf(-q, d.s, x);
-      return e == 0.0f ? q : __builtin_fmaf(e, d.r, q);
-    }
-  }
-  return x / d.s;
+  return div_fast_ok(x, d) ? div_fast(x, d) : x / d.s;
 }
 
 }  // namespace pa
