@@ -101,6 +101,16 @@ __global__ __launch_bounds__(256) void kv_write_tokens_kernel(const WriteArgs a)
 // goes to its own slot.
 constexpr int kRowTokens = 64;
 
+// Element index of (dimension d, token tok) in the LDS transpose: [D][64],
+// each row rotated by 4 (d / 8) tokens. A chunk's writes put the 8 dimensions
+// ch*8 .. ch*8+7 of one token, and the lanes of a wave hold 16 (or 8) chunks
+// ch of the same token: unrotated, those land 512 bytes apart, all in one LDS
+// bank; the rotation spreads them over 16 banks. Rotations are whole dwords,
+// so a dword of the row still holds consecutive tokens.
+__device__ __forceinline__ int vt_pos(int d, int tok) {
+  return d * kRowTokens + ((tok + 4 * (d >> 3)) & (kRowTokens - 1));
+}
+
 template <int ST, int FMT, int D>
 __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   constexpr int cpt = D / 8;                        // 16-byte source chunks per token
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
     const uint32_t vw[4] = {vc[it].x, vc[it].y, vc[it].z, vc[it].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint8_t* cell = vt + ((ch * 8 + e) * kRowTokens + tok) * ES;
+      uint8_t* cell = vt + vt_pos(ch * 8 + e, tok) * ES;
       if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(cell) = (uint16_t)(vw[e >> 1] >> ((e & 1) * 16));
       else *cell = (uint8_t)(vw[e >> 2] >> ((e & 3) * 8));
     }
@@ -180,9 +190,17 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
     const int64_t ph = (s0 >> a.bs_log2) * a.num_kv_heads + h;
     uint8_t* vdst = a.value_cache +
         (((ph << (a.bs_log2 - 6)) + ((s0 & bs_mask) >> 6)) * D) * kRowTokens * ES;
-    const int n16 = D * kRowTokens * ES / 16;
-    for (int f = threadIdx.x; f < n16; f += 256)
-      reinterpret_cast<u32x4*>(vdst)[f] = reinterpret_cast<const u32x4*>(vt)[f];
+    constexpr int per_row = kRowTokens * ES / 16;   // 16-byte chunks per dimension row
+    constexpr int tpd = 4 / ES;                      // tokens per dword
+    const int n16 = D * per_row;
+    for (int f = threadIdx.x; f < n16; f += 256) {
+      const int d = f / per_row, tok = (f - d * per_row) * (16 / ES);
+      uint32_t w4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w4[q] = *reinterpret_cast<const uint32_t*>(vt + vt_pos(d, tok + q * tpd) * ES);
+      reinterpret_cast<u32x4*>(vdst)[f] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
   } else {
     const int vg_log2 = a.bs_log2 < 6 ? a.bs_log2 : 6;
     const int T = 1 << vg_log2;
@@ -195,8 +213,9 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
       const int off = (int)(slot & bs_mask);
       uint8_t* vdst = a.value_cache +
           ((((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D + d) * T + (off & (T - 1))) * ES;
-      if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(vdst) = *reinterpret_cast<const uint16_t*>(vt + f * 2);
-      else *vdst = vt[f];
+      const int idx = vt_pos(d, tok);
+      if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(vdst) = *reinterpret_cast<const uint16_t*>(vt + idx * 2);
+      else *vdst = vt[idx];
     }
   }
 }
