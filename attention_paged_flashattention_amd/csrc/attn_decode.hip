@@ -18,7 +18,7 @@
 //   dequantizes them in registers; no other wave reads a tile. Decode (one
 //   16-row block) keeps two tiles in registers. The verify groups (two or
 //   four row blocks) have registers for one tile only: their loads go from
-//   HBM straight into two wave-private LDS slots (global -> LDS copies, two
+//   HBM straight into two wave-private LDS slots (buffer -> LDS copies, two
 //   tiles ahead) and come back into registers when the tile's turn comes.
 //   Keys are dealt to MFMA rows so that each lane's S^T outputs are
 //   exactly the 16 keys it later feeds as the B operand of O^T += V^T P^T --
@@ -91,8 +91,8 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kWaitVmcnt0 = 0x0F70;
 // Growth of the running max (log2 units) tolerated before O and l are rescaled.
 constexpr float kRescaleSlackD = 8.0f;
-// Cache policy of the global -> LDS copies of the KV stream: non-temporal
-// (the "nt" bit, as the streaming register loads use), read once.
+// Cache policy of the K/V stream loads (registers and LDS copies): non-temporal
+// (the "nt" bit), read once.
 constexpr int kStreamPolicy = 2;
 
 // Raw cache bytes of one 64-key tile as one lane holds them.
@@ -242,7 +242,7 @@ struct DecodePipe {
 // LDS-staged pipeline for the wider row groups (FP8 cache, two or four 16-row
 // blocks, pages of >= 64 keys so that page ids are scalar loads), whose
 // registers hold one tile but not two: each wave's tiles are
-// copied from HBM straight into two wave-private LDS slots (global -> LDS
+// copied from HBM straight into two wave-private LDS slots (buffer -> LDS
 // loads, no registers in flight), two tiles ahead of the one being
 // multiplied, and read back into registers when their turn comes.
 template <int FMT, int NQB, bool UNI>
@@ -410,7 +410,7 @@ void decode_split_kernel(const DecodeArgs a) {
       }
   };
 
-  // LDS pipeline: the same 128-bit loads as load(), each one a global -> LDS
+  // LDS pipeline: the same 128-bit loads as load(), each one a buffer -> LDS
   // copy of 16 bytes per lane (lane i's bytes land at offset 16 i of the
   // load's 1 KB block of the slot), and the read-back that gives every lane
   // exactly the words load() would have given it.
@@ -451,7 +451,7 @@ void decode_split_kernel(const DecodeArgs a) {
   };
 
   // The read-back is one asm block that ends with its own wait for the
-  // reads: the compiler cannot tell which slot a pending global -> LDS copy
+  // reads: the compiler cannot tell which slot a pending buffer -> LDS copy
   // writes, and before reads it can see it waits for every copy in flight
   // (the next tiles' too), which would drain the pipeline each tile. The
   // explicit waits in the main loop order the copies before these reads.
@@ -680,7 +680,7 @@ void decode_split_kernel(const DecodeArgs a) {
     // Tile j sits in slot j % 2; once it is back in registers the slot takes
     // tile j + 2 (past the last tile, a cache-hit copy that is never read:
     // every iteration issues the same loads), so two tiles stream in while
-    // one is multiplied. The compiler does not order the global -> LDS
+    // one is multiplied. The compiler does not order the buffer -> LDS
     // copies before the reads of their slot, so each read is preceded by an
     // explicit wait: issued after tile j's copies are exactly the next
     // tile's copies (page ids are scalar loads), so waiting until that many
