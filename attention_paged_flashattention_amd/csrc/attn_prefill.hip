@@ -14,10 +14,11 @@
 //   heads: with round-robin dispatch over the 8 XCDs, each XCD's L2 holds the
 //   K/V of one head while all its work-groups stream it. Query tiles with the
 //   most keys are dispatched first.
-// * Keys are walked in 64-key tiles. The 512 threads load the FP8 tile with
-//   128-bit loads (one page id per tile), dequantize in registers and store
-//   16-bit K (token-major) and V (dimension-major) tiles in LDS, three
-//   buffers deep; loads run three tiles ahead of the tile being multiplied.
+// * Keys are walked in 64-key tiles. Waves 0-3 load the FP8 tile with 128-bit
+//   loads (one page id per tile), dequantize in registers and store 16-bit K
+//   (token-major) and V (dimension-major) tiles in LDS, three buffers deep;
+//   loads run three tiles ahead of the tile being multiplied. (16-bit caches
+//   are staged by all 8 waves, 16 bytes of K and of V each.)
 // * Ping-pong: waves 0-3 and 4-7 share the SIMDs and cross the same two
 //   barriers per tile doing opposite work, so one wave's softmax (VALU) runs
 //   under the other wave's MFMAs.
@@ -72,8 +73,14 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int KS = D / 16;              // QK k-steps (16 dims each)
   constexpr int DBLK = D / 32;            // 32-dim output blocks
   constexpr int NT = kPrefillThreads;
+  // Staging threads: with FP8 caches only waves 0-3 load and dequantize the
+  // tile. A wave that issues a tile's loads stalls on them for a few hundred
+  // cycles (the loads miss L1); confined to one group, that stall falls at the
+  // top of the group's softmax phase and the other group's matrix phase starts
+  // without it.
+  constexpr int NSTAGE_T = ES == 1 ? NT / 2 : NT;
   // elements per staging thread per tile (K and V): at least one 16-byte load
-  constexpr int EPT = (BN * D / NT) * ES >= 16 ? BN * D / NT : 16 / ES;
+  constexpr int EPT = (BN * D / NSTAGE_T) * ES >= 16 ? BN * D / NSTAGE_T : 16 / ES;
   constexpr int NSTAGE = BN * D / EPT;    // staging threads (whole waves)
   constexpr int TPK = D / EPT;            // threads per key row
   constexpr int TPR = BN / EPT;           // threads per value row (dimension)
@@ -152,7 +159,7 @@ void prefill_kernel(const PrefillArgs a) {
       qop[ks] = rvalid ? __builtin_bit_cast(OpT, ld16(qp + 16 * ks)) : OpT{};
   }
 
-  // ---- global -> register staging (all 512 threads) ----
+  // ---- global -> register staging (threads below NSTAGE) ----
   // K: thread owns key kt, dims kd0 .. kd0 + EPT - 1.
   // V: thread owns dim vd, keys vk0 .. vk0 + EPT - 1.
   // Every staging thread issues the same loads for every tile, whatever the
