@@ -27,10 +27,13 @@
 //   and 3 of the row index swapped, which makes each lane's S^T outputs the
 //   8-key runs that the PV step needs as its B operand: P never leaves the
 //   lane, and the V^T operand is one 16-byte LDS read.
-// * Online softmax in exp2 units, the row max reduced between the two lanes
-//   that share a row; O is rescaled only when a row's max grows by more than
-//   2^8 (wave vote), so most tiles skip the rescale; only tiles that cross the
-//   causal diagonal are masked.
+// * Online softmax in exp2 units against a running reference max that may lag
+//   the row max by up to 2^8: P is formed against it directly, and only when
+//   a lane's partial row sum shows that some p could exceed 2^8 (wave vote)
+//   is the tile's row max taken (reduced between the two lanes that share a
+//   row) and, if it outgrew the reference, O rescaled and P formed again;
+//   most tiles need no max at all. Only tiles that cross the causal diagonal
+//   are masked.
 // * P is rounded to fp16 (V from FP8 is exact in fp16) and O^T += V^T P^T runs
 //   on v_mfma_f32_32x32x16_f16.
 #include "pa_device.h"
@@ -56,6 +59,8 @@ __device__ __forceinline__ f32x16 mfma32_qk(typename QOp32<QT>::T a, typename QO
 constexpr float kNegInfP = -__builtin_inff();
 // Growth of the running max (log2 units) tolerated before O and l are rescaled.
 constexpr float kRescaleSlack = 8.0f;
+// Partial row sum of one tile's P below which no lane's p can exceed 2^8.
+constexpr float kPSumMax = 256.0f;
 
 // MFMA row R of a 32-key block holds key kappa(R): bits 2 and 3 swapped.
 __device__ __forceinline__ int kappa(int R) {
@@ -332,48 +337,68 @@ void prefill_kernel(const PrefillArgs a) {
           if (key > rpos || key >= ctx) sacc[mb][j] = kNegInfP;
         }
     }
-    float tm = kNegInfP;
+    // P = 2^(s*C - m) against the running reference m, into fp16, and this
+    // lane's partial row sum of the fp16 values (two per dot2).
+    auto exp_sum = [&]() __attribute__((always_inline)) -> float {
+      const float muse = m == kNegInfP ? 0.0f : m;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sacc[mb][j]);
-    tm = swap_max<32>(tm);
-    // Lazy rescaling: O and l are kept relative to a running max m that is
-    // raised only when some row of the wave sees a max larger than m + 8
-    // (log2 units). p = 2^(s*C - m) then stays <= 2^8 (fine in fp16), and O/l
-    // is unchanged because both carry the same reference.
-    const float mcand = fmaxf(m, tm * C);
-    if (__any(mcand > m + kRescaleSlack)) {
-      const float alpha = mcand == kNegInfP ? 1.0f : __builtin_amdgcn_exp2f(m - mcand);
-      m = mcand;
-      l *= alpha;
+        for (int j = 0; j < 16; ++j) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][j], C, -muse));
+          pop[mb * 2 + (j >> 3)][j & 7] = (_Float16)pv;
+        }
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+      float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
-    }
-    const float muse = m == kNegInfP ? 0.0f : m;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][j], C, -muse));
-        pop[mb * 2 + (j >> 3)][j & 7] = (_Float16)pv;
+      for (int i = 0; i < 4; ++i) {
+        // (vector elements are copied to scalars before the bit casts: this
+        // compiler reads element 0 when a bit cast takes a vector element)
+        const u32x4 w = __builtin_bit_cast(u32x4, pop[i]);
+        const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+        ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w0), one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w1), one, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w2), one, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w3), one, ps1, false);
       }
-    // the row sum adds the fp16 P that the PV product uses, two per dot2
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    float ps0 = 0.0f, ps1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // (vector elements are copied to scalars before the bit casts: this
-      // compiler reads element 0 when a bit cast takes a vector element)
-      const u32x4 w = __builtin_bit_cast(u32x4, pop[i]);
-      const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-      ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w0), one, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w1), one, ps1, false);
-      ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w2), one, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w3), one, ps1, false);
+      return ps0 + ps1;
+    };
+    // Lazy rescaling without a per-tile max in the common case: O and l are
+    // kept relative to a running reference m that lags the row max by at most
+    // 8 (log2 units), so every p <= 2^8 (fine in fp16) and O/l is unchanged
+    // by the choice of reference. P is first formed against m directly; each
+    // p is at most the lane's partial sum, so sums <= 2^8 in every lane
+    // settle the tile. Otherwise (and on a row's first tile) the tile's row
+    // max is taken, m, O and l are moved to it if it exceeds m + 8 somewhere
+    // in the wave, and P is formed again.
+    const bool fresh = __any(m == kNegInfP);
+    float lt = 0.0f;
+    bool settled = false;
+    if (!fresh) {
+      lt = exp_sum();
+      settled = !__any(!(lt <= kPSumMax));
     }
-    l += ps0 + ps1;
+    if (!settled) {
+      float tm = kNegInfP;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) tm = fmaxf(tm, sacc[mb][j]);
+      tm = swap_max<32>(tm);
+      const float mcand = fmaxf(m, tm * C);
+      if (__any(mcand > m + kRescaleSlack)) {
+        const float alpha = mcand == kNegInfP ? 1.0f : __builtin_amdgcn_exp2f(m - mcand);
+        m = mcand;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+      }
+      // (P is formed again even when m did not move: keeping the first pass's
+      // P alive across the max costs more registers than this rare pass)
+      lt = exp_sum();
+    }
+    l += lt;
   };
 
   // O^T += V^T P^T with V from buffer vb, operands read PF ahead.

@@ -32,6 +32,16 @@ def _cache_np(t):
     return t.cpu().numpy()
 
 
+def _ramp_keys(case, ramp):
+    """Scale each key row by ramp[position] (one sequence), keeping the cache
+    format's per-head scales consistent with the new keys."""
+    kf = synth.to_f32(case.k, case.kv_dtype) * ramp[:, None, None].astype(np.float32)
+    case.k = synth.round_to(kf, case.kv_dtype)
+    if case.cache_fmt == "e4m3":
+        case.k_scale = synth.head_scales(case.k, case.kv_dtype)
+    return case
+
+
 # ---------------------------------------------------------------------------
 # quantize-on-write: bit-exact against the oracle, whole caches compared
 # ---------------------------------------------------------------------------
@@ -218,6 +228,30 @@ def test_verify_parity_lds_pipeline(runner, fmt, B, ctx, q_len, bs, parts, q_dty
     check_close(out, ref, fmt, "verify f32")
 
 
+@pytest.mark.parametrize("fmt,q_len,bs,parts,q_dtype", [
+    ("e4m3", 1, 2048, 4, "f16"),     # decode, register pipeline
+    ("e5m2", 4, 16, 3, "f16"),       # per-lane page ids
+    ("e4m3", 16, 64, 4, "bf16"),     # four row blocks, LDS pipeline
+    ("e5m2", 8, 2048, 0, "f16"),     # default partitioning
+])
+def test_verify_scores_that_jump(runner, fmt, q_len, bs, parts, q_dtype):
+    """Keys whose scores keep rising along the context (by ~100 in log2
+    units), jump in one run of keys and fall back: each wave's running
+    reference is raised in the middle of its tiles (see the prefill test)."""
+    ctx = 3000
+    case = _mk(fmt, 1, (ctx,), q_len, 32, 8, 128, bs, q_dtype)
+    ramp = 1.0 + np.arange(ctx) / 150.0
+    ramp[1700:1760] = 40.0
+    case = _ramp_keys(case, ramp)
+    log(f"verify with rising scores: {fmt} q_len={q_len} bs={bs} P={parts} q={q_dtype}")
+    dc = runner.DeviceCase(case)
+    dc.write_all()
+    out = dc.verify(q_len, num_partitions=parts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle_full(case).reshape(1, q_len, 32, 128)
+    check_close(out, ref, fmt, "verify rising scores f32")
+
+
 def test_verify_rows_equal_decodes(runner):
     """The grouped verifier is exact: row i equals a decode at ctx - q_len + 1 + i
     (same kernels, so compared within fp32 rounding of the partition merge)."""
@@ -310,6 +344,27 @@ def test_prefill_chunked_parity(runner, fmt, total, chunk, Hq, Hkv, D, bs, q_dty
     out = torch.cat(outs, 0)
     torch.cuda.synchronize()
     check_close(out, ref, fmt, "prefill f32")
+
+
+@pytest.mark.parametrize("fmt,bs,q_dtype", [("e4m3", 2048, "bf16"), ("e5m2", 16, "f16")])
+def test_prefill_scores_that_jump(runner, fmt, bs, q_dtype):
+    """Scores whose row max keeps rising along the keys (by ~100 in log2
+    units over the sequence), jumps in one run of keys and falls back: the
+    softmax's running reference must be raised in the middle of the walk,
+    many times per row, and later tiles far below it must not disturb it."""
+    total = 1200
+    case = _mk(fmt, 1, (total,), total, 32, 8, 128, bs, q_dtype)
+    ramp = 1.0 + np.arange(total) / 60.0
+    ramp[700:760] = 40.0
+    case = _ramp_keys(case, ramp)
+    log(f"prefill with rising scores: {fmt} bs={bs} q={q_dtype}")
+    dc = runner.DeviceCase(case)
+    ref = oracle_full(case)
+    outs = [dc.prefill_chunk(s, min(total, s + 400), out_dtype=torch.float32)
+            for s in range(0, total, 400)]
+    out = torch.cat(outs, 0)
+    torch.cuda.synchronize()
+    check_close(out, ref, fmt, "prefill rising scores f32")
 
 
 def test_prefill_batched_varlen(runner):
