@@ -147,7 +147,9 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
     sl[it] = a.slots[t];
   }
   const int64_t s0 = ld_const(a.slots, t0);
-  const int64_t my_slot = a.slots[t0 + min(i, ntok - 1)];
+  // the slot of token i % 64: the one token whose value codes this thread
+  // stores when the slots are not one contiguous group (256 threads, 64 tokens)
+  const int64_t my_slot = a.slots[t0 + min(i & (kRowTokens - 1), ntok - 1)];
   // All loaded values are consumed here (an empty asm statement), so the
   // compiler waits for them once and cannot sink a load into the conditional
   // key store that alone uses it. Then all conversions, then the stores.
@@ -204,18 +206,19 @@ __global__ __launch_bounds__(256) void kv_write_rows_kernel(const WriteArgs a) {
   } else {
     const int vg_log2 = a.bs_log2 < 6 ? a.bs_log2 : 6;
     const int T = 1 << vg_log2;
-    for (int f = threadIdx.x; f < D * kRowTokens; f += 256) {
-      const int d = f / kRowTokens, tok = f - d * kRowTokens;
-      if (tok >= ntok) continue;
-      const int64_t slot = a.slots[t0 + tok];
-      if (slot < 0) continue;
-      const int64_t ph = (slot >> a.bs_log2) * a.num_kv_heads + h;
-      const int off = (int)(slot & bs_mask);
-      uint8_t* vdst = a.value_cache +
-          ((((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D + d) * T + (off & (T - 1))) * ES;
-      const int idx = vt_pos(d, tok);
-      if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(vdst) = *reinterpret_cast<const uint16_t*>(vt + idx * 2);
-      else *vdst = vt[idx];
+    static_assert(256 % kRowTokens == 0, "a thread keeps one token");
+    const int tok = i & (kRowTokens - 1);
+    if (tok < ntok && my_slot >= 0) {
+      const int64_t ph = (my_slot >> a.bs_log2) * a.num_kv_heads + h;
+      const int off = (int)(my_slot & bs_mask);
+      uint8_t* vbase = a.value_cache +
+          (((ph << (a.bs_log2 - vg_log2)) + (off >> vg_log2)) * D * T + (off & (T - 1))) * ES;
+      for (int d = i / kRowTokens; d < D; d += 256 / kRowTokens) {
+        const int idx = vt_pos(d, tok);
+        uint8_t* vdst = vbase + (int64_t)d * T * ES;
+        if constexpr (ES == 2) *reinterpret_cast<uint16_t*>(vdst) = *reinterpret_cast<const uint16_t*>(vt + idx * 2);
+        else *vdst = vt[idx];
+      }
     }
   }
 }
