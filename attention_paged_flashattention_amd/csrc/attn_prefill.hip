@@ -471,19 +471,63 @@ void prefill_kernel(const PrefillArgs a) {
   if (n < ntiles) iteration(n, R1, R0);
   if (grp_b) pv((ntiles - 1) % NBUF);
 
-  // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r].
+  // Epilogue: lane holds O^T[d = 32 db + 8 (j/4) + 4 hgrp + j%4][row r]. The
+  // normalised rows go through LDS (the tile buffers, free after the last PV)
+  // so that they leave as 16-byte runs of a row: stored straight from the
+  // MFMA layout, each store instruction would write 2 or 4 bytes to each of
+  // 64 rows, and the wave would stall issuing 64 of them.
   l = swap_sum<32>(l);
-  if (!rvalid) return;
   const float vscale = (a.v_scale ? ld_const(a.v_scale, g) : 1.0f) * kv_fold<FMT>();
-  const float f = l > 0.0f ? vscale / l : 0.0f;
-  const int64_t obase = ((int64_t)(q0 + tok0 + rtok) * a.num_q_heads + rh) * D;
+  const float f = (rvalid && l > 0.0f) ? vscale / l : 0.0f;
+  constexpr int OES = OT == O_F32 ? 4 : 2;             // output element bytes
+  // dimensions per pass: rows of at most 256 bytes, four waves' rows within
+  // each tile array
+  constexpr int LIMB = (int)((sizeof(sk) < sizeof(sv) ? sizeof(sk) : sizeof(sv)) / 128) - 16;
+  constexpr int DH0 = 256 / OES < D ? 256 / OES : D;
+  constexpr int DH = DH0 * OES <= LIMB ? DH0 : DH0 / 2;
+  constexpr int RSTRIDE = DH * OES + 16;               // LDS row stride (bytes)
+  constexpr int CPR = DH * OES / 16;                   // 16-byte chunks per row
+  static_assert(4 * 32 * RSTRIDE <= (int)sizeof(sk) && 4 * 32 * RSTRIDE <= (int)sizeof(sv) &&
+                (32 * CPR) % 64 == 0 && D % DH == 0, "four waves' rows fit in each tile array");
+  uint8_t* stage = (w < 4 ? reinterpret_cast<uint8_t*>(&sk[0][0])
+                          : reinterpret_cast<uint8_t*>(&sv[0][0])) + (w & 3) * 32 * RSTRIDE;
+  uint8_t* const outb = reinterpret_cast<uint8_t*>(a.out);
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
+  for (int pass = 0; pass < D / DH; ++pass) {
+    __syncthreads();   // the tile buffers (or the previous pass's rows) are no longer read
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int d = 32 * db + 8 * (j >> 2) + 4 * hgrp + (j & 3);
-      store_out<OT>(a.out, obase + d, oacc[db][j] * f);
+    for (int db = pass * DH / 32; db < (pass + 1) * DH / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = 32 * db + 8 * jj + 4 * hgrp - pass * DH;
+        uint8_t* dst = stage + c32 * RSTRIDE + col * OES;
+        const float v0 = oacc[db][4 * jj] * f, v1 = oacc[db][4 * jj + 1] * f;
+        const float v2 = oacc[db][4 * jj + 2] * f, v3 = oacc[db][4 * jj + 3] * f;
+        if constexpr (OT == O_F32) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+        } else if constexpr (OT == O_F16) {
+          const _Float16 h[4] = {(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+          *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, h);
+        } else {
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{(uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16),
+                    (uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16)};
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 32 * CPR / 64; ++k) {
+      const int idx = k * 64 + lane;
+      const int rr = idx / CPR, ch = idx % CPR;
+      const int r2 = w * 32 + rr;
+      const int tk = r2 / G;
+      if (tk < ntok) {
+        const int64_t row = (int64_t)(q0 + tok0 + tk) * a.num_q_heads + g * G + r2 % G;
+        *reinterpret_cast<u32x4*>(outb + (row * D + pass * DH) * OES + ch * 16) =
+            *reinterpret_cast<const u32x4*>(stage + rr * RSTRIDE + ch * 16);
+      }
     }
+  }
 }
 
 template <int D, int FMT, int QT>
