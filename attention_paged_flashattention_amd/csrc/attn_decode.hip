@@ -86,6 +86,7 @@ __device__ __forceinline__ half8 val_op(const uint32_t* dw) {
 }
 
 constexpr float kNegInf = -__builtin_inff();
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -270,14 +271,15 @@ void decode_split_kernel(const DecodeArgs a) {
   constexpr int TILE_BYTES = TILE_LOADS * 1024;
   // LDS: the two tile slots of each wave (LDS pipeline) and, after the main
   // loop, the buffers that merge the 4 waves' states (in the slots' space)
-  constexpr int MERGE_FLOATS = 4 * D * 17 + 2 * 4 * 16;
+  constexpr int MERGE_FLOATS = 4 * D * 17 + 2 * NQB * 4 * 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds_slots[LPIPE ? 2 * 4 * TILE_BYTES : 1];
   __shared__ float sm_own[LPIPE ? 1 : MERGE_FLOATS];
   static_assert(!LPIPE || 2 * 4 * TILE_BYTES >= MERGE_FLOATS * 4, "merge buffers fit");
   float* sm_base = LPIPE ? reinterpret_cast<float*>(lds_slots) : sm_own;
   auto sm_o = reinterpret_cast<float (*)[D][17]>(sm_base);
-  auto sm_m = reinterpret_cast<float (*)[16]>(sm_base + 4 * D * 17);
-  auto sm_l = reinterpret_cast<float (*)[16]>(sm_base + 4 * D * 17 + 4 * 16);
+  // per 16-row block: each wave's (max, sum) of its rows, kept for the stores
+  auto sm_m = reinterpret_cast<float (*)[4][16]>(sm_base + 4 * D * 17);
+  auto sm_l = reinterpret_cast<float (*)[4][16]>(sm_base + 4 * D * 17 + NQB * 4 * 16);
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -723,53 +725,86 @@ void decode_split_kernel(const DecodeArgs a) {
   const int64_t P = a.num_parts;
   [[maybe_unused]] const float vscale =
       ONEP ? (a.v_scale ? ld_const(a.v_scale, g) : 1.0f) * kv_fold<FMT>() : 0.0f;
+  // Thread t merges 4 consecutive dimensions of a row (D / 4 threads per row,
+  // 256 / (D / 4) rows per pass) and keeps them in registers until every
+  // block is merged: the stores then go out as 16-byte runs after the last
+  // barrier. (Four-byte stores from inside each block's merge took most of
+  // the merge's time: a wave stalls issuing each store, and the next
+  // barrier waits for them.)
+  constexpr int GPR = D / 4;                 // 4-dimension groups per row
+  constexpr int RPP = 256 / GPR;             // rows per pass
+  constexpr int PASSES = 16 / RPP;           // passes per 16-row block
+  static_assert(RPP * PASSES == 16, "whole rows per pass");
+  const int d0 = 4 * (threadIdx.x % GPR);
+  f32x4 res[NQB][PASSES];
+  float resm[NQB][PASSES], resl[NQB][PASSES];
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     float lf = l[nb];
     lf = swap_sum<32>(swap_sum<16>(lf));
     if (qg == 0) {
-      sm_m[w][c] = m[nb];
-      sm_l[w][c] = lf;
+      sm_m[nb][w][c] = m[nb];
+      sm_l[nb][w][c] = lf;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm_o[w][db * 16 + 4 * qg + i][c] = o[nb][db][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < 16 * D; e += 256) {
-      const int d = e % D, cc = e / D;
-      const int r = nb * 16 + cc;
-      if (r >= rows) continue;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int cc = ps * RPP + threadIdx.x / GPR;
+      if (nb * 16 + cc >= rows) continue;
       float M = kNegInf;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][cc]);
-      float acc = 0.0f, lt = 0.0f;
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[nb][ww][cc]);
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      float lt = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) {
-        const float mw = sm_m[ww][cc];
+        const float mw = sm_m[nb][ww][cc];
         if (mw == kNegInf) continue;
         const float wt = __builtin_amdgcn_exp2f(mw - M);
-        acc += wt * sm_o[ww][d][cc];
-        lt += wt * sm_l[ww][cc];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += wt * sm_o[ww][d0 + i][cc];
+        lt += wt * sm_l[nb][ww][cc];
       }
+      if constexpr (ONEP) acc *= lt > 0.0f ? vscale / lt : 0.0f;
+      res[nb][ps] = acc;
+      resm[nb][ps] = M;
+      resl[nb][ps] = lt;
+    }
+    if (nb + 1 < NQB) __syncthreads();   // sm_o is rewritten by the next block
+  }
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int cc = ps * RPP + threadIdx.x / GPR;
+      const int r = nb * 16 + cc;
+      if (r >= rows) continue;
       const int qi = r / G, h = g * G + r % G;
       const int64_t rowg = (int64_t)(b * a.q_len + qi) * a.num_q_heads + h;
+      const f32x4 v = res[nb][ps];
       if constexpr (ONEP) {
-        const float f = lt > 0.0f ? vscale / lt : 0.0f;
-        const int64_t idx = rowg * D + d;
-        if (a.out_type == O_F32) store_out<O_F32>(a.out, idx, acc * f);
-        else if (a.out_type == O_F16) store_out<O_F16>(a.out, idx, acc * f);
-        else store_out<O_BF16>(a.out, idx, acc * f);
+        const int64_t idx = rowg * D + d0;
+        if (a.out_type == O_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + idx) = v;
+        } else if (a.out_type == O_F16) {
+          const _Float16 hv[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + idx) =
+              __builtin_bit_cast(u32x2, hv);
+        } else {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + idx) =
+              u32x2{(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                    (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+        }
         continue;
       }
-      a.ws_o[(rowg * P + p) * D + d] = acc;
-      if (d == 0) {
-        a.ws_ml[(rowg * P + p) * 2] = M;
-        a.ws_ml[(rowg * P + p) * 2 + 1] = lt;
-      }
+      *reinterpret_cast<f32x4*>(a.ws_o + (rowg * P + p) * D + d0) = v;
+      if (d0 == 0)
+        *reinterpret_cast<f32x2*>(a.ws_ml + (rowg * P + p) * 2) = f32x2{resm[nb][ps], resl[nb][ps]};
     }
-    __syncthreads();
-  }
 }
 
 // One work-group of 256 threads per output row:

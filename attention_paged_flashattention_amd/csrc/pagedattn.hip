@@ -100,6 +100,8 @@ pa_status check_common(const void* q, pa_dtype q_dtype, const void* kc, const vo
                        float softmax_scale, const void* out, pa_dtype out_dtype) {
   if (!q || !kc || !vc || !block_tables || !context_lens || !out)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if (hq <= 0 || hkv <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
       max_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive");

@@ -44,14 +44,16 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless marked (host). Tensors are dense,
- *     row-major, in the shapes stated. The library never allocates or frees
+ *     row-major, in the shapes stated; attention outputs (out) start on a
+ *     16-byte boundary (rows leave as 16-byte runs). The library never allocates or frees
  *     device memory and keeps no pointer after a call returns.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     runs asynchronously. No call synchronizes, reads device memory from the
  *     host or allocates, so the calls may be captured into a HIP graph.
  *   - Arguments the host can check are checked before anything is launched:
  *     PA_ERR_INVALID_ARG for null pointers, non-positive sizes, num_q_heads not
- *     a multiple of num_kv_heads, missing E4M3 scales, too small a workspace;
+ *     a multiple of num_kv_heads, missing E4M3 scales, too small a workspace,
+ *     a misaligned workspace or output;
  *     PA_ERR_UNSUPPORTED for well-formed shapes no kernel covers (see
  *     pa_supports), so the caller can fall back. PA_ERR_HIP reports a launch
  *     error. pa_last_error() describes the last failure on the calling thread.

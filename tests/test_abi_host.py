@@ -108,6 +108,7 @@ def _call_verify(pa, q_len, **kw):
     (dict(ws=NUL), 1),
     (dict(wsb=16), 1),
     (dict(ws=ctypes.c_void_p(0x1010)), 1),   # misaligned workspace
+    (dict(out=ctypes.c_void_p(0x1008)), 1),  # output not on a 16-byte boundary
     (dict(hq=128, hkv=1), 2),                # G = 128 rows exceed one decode group
     (dict(batch=65536), 2),                  # a launch dimension
 ])
@@ -167,6 +168,7 @@ def test_prefill_rejects_before_launch(pa):
     assert call(cu=NUL) == 1
     assert call(maxq=5000) == 1
     assert call(hq=65, hkv=1) == 2           # G = 65 > 64
+    assert call(out=ctypes.c_void_p(0x1002)) == 1   # output not on a 16-byte boundary
     assert call(B=-1) == 1
     assert call(B=0) == 0
     assert call(totq=0) == 0
