@@ -584,6 +584,29 @@ void decode_split_kernel(const DecodeArgs a) {
         for (int nb = 0; nb < NQB; ++nb) sacc[nb][s] = mfma_qk<QT>(kop, qop[nb][kk], sacc[nb][s]);
       }
     }
+    // Each lane's maximum over its 16 scores per block. With two or more
+    // blocks it is taken in the same stretch as the products (its first terms
+    // are ready before the last products are; measured: q8 +3%, the draft
+    // window +2-10%), and again after masking on the few tiles that mask; the
+    // empty asm keeps the compiler from sinking the first one past the branch.
+    // One block takes it after the mask (the same order measured no faster).
+    auto lane_max = [&](int nb) {
+      float tm = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sacc[nb][s][i]);
+      return tm;
+    };
+    constexpr bool kEarlyMax = NQB >= 2;
+    float tmax[NQB];
+    if constexpr (kEarlyMax) {
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        tmax[nb] = lane_max(nb);
+        asm volatile("" : "+v"(tmax[nb]));
+      }
+    }
     if (nm) {
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
@@ -598,7 +621,12 @@ void decode_split_kernel(const DecodeArgs a) {
             const int key = t0 + 16 * qg + 4 * s + i;
             if (key > lim_hi || key < lim_lo) sacc[nb][s][i] = kNegInf;
           }
+        if constexpr (kEarlyMax) tmax[nb] = lane_max(nb);
       }
+    }
+    if constexpr (!kEarlyMax) {
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) tmax[nb] = lane_max(nb);
     }
     // Lazy rescaling (see the prefill kernel): the reference max is raised
     // only when some row's max exceeds it by more than 2^8. Every block's
@@ -610,12 +638,7 @@ void decode_split_kernel(const DecodeArgs a) {
     bool any_grow = false;
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
-      float tm = kNegInf;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sacc[nb][s][i]);
-      tm = swap_max<32>(swap_max<16>(tm));
+      const float tm = swap_max<32>(swap_max<16>(tmax[nb]));
       mcand[nb] = fmaxf(m[nb], tm * C);
       grow[nb] = __any(mcand[nb] > m[nb] + kRescaleSlackD);
       any_grow |= grow[nb];
