@@ -416,21 +416,17 @@ void decode_split_kernel(const DecodeArgs a) {
   // copy of 16 bytes per lane (lane i's bytes land at offset 16 i of the
   // load's 1 KB block of the slot), and the read-back that gives every lane
   // exactly the words load() would have given it.
-  // Copies for a tile j >= J (issued only to keep the number of loads per
-  // iteration fixed) all read the first 16 bytes of the group's first query
-  // row, which this wave has just loaded (a cache hit, no HBM traffic); the
-  // slot they fill is never read.
-  [[maybe_unused]] const uint8_t* dummy = reinterpret_cast<const uint8_t*>(
-      a.q + ((int64_t)b * a.q_len * a.num_q_heads + (int64_t)g * G) * D);
+  // Only real tiles are copied (j < J): where no next tile was issued, the
+  // loop waits for all copies instead of all but the next tile's. Each lane's
+  // offset is one register per tile for K and one for the whole loop for V;
+  // the constant part of each copy's offset goes in its scalar offset.
   [[maybe_unused]] auto dma = [&](uint8_t* slot, int j, const TilePages& pg) {
     // buffer copies from the page base (the LDS pipeline runs with pages of
-    // >= 64 keys only), as in load(); a dummy copy reads offset 0 of a
-    // descriptor over the query row
-    const bool real = j < J;
+    // >= 64 keys only), as in load()
     const int t0 = tile_t0(j);
     const uint8_t* kb = a.key_cache + ((pg.k * kv_heads + g) << bs_log2) * (int64_t)(D * ES);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(real ? kb : dummy);
-    const int ko = real ? ((((t0 + 16 * (c >> 2)) & bs_mask) + (c & 3)) * D + RUN * qg) * ES : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb);
+    const int ko = ((((t0 + 16 * (c >> 2)) & bs_mask) + (c & 3)) * D + RUN * qg) * ES;
     int n = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -438,18 +434,18 @@ void decode_split_kernel(const DecodeArgs a) {
       for (int x = 0; x < KDW / 4; ++x, ++n)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kr, (__attribute__((address_space(3))) void*)(slot + n * 1024), 16,
-            real ? ko + 4 * s * D * ES + 16 * x : 0, 0, 0, kStreamPolicy);
+            ko, 4 * s * D * ES + 16 * x, 0, kStreamPolicy);
     const uint8_t* vb = a.value_cache +
         ((((pg.v * kv_heads + g) << (bs_log2 - 6)) + ((t0 & bs_mask) >> 6)) * D << 6) * (int64_t)ES;
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(real ? vb : dummy);
-    const int vo = real ? ((c << 6) | (16 * qg)) * ES : 0;
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb);
+    const int vo = ((c << 6) | (16 * qg)) * ES;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int x = 0; x < VDW / 4; ++x, ++n)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             vr, (__attribute__((address_space(3))) void*)(slot + n * 1024), 16,
-            real ? vo + ((db * 16) << 6) * ES + 16 * x : 0, 0, 0, kStreamPolicy);
+            vo, ((db * 16) << 6) * ES + 16 * x, 0, kStreamPolicy);
   };
 
   // The read-back is one asm block that ends with its own wait for the
@@ -529,14 +525,13 @@ void decode_split_kernel(const DecodeArgs a) {
   }
 
   if constexpr (LPIPE) {
-    // tiles 0 and 1 into the wave's two slots (tile 1 a dummy copy when
-    // J = 1: the same number of loads whatever J is), with tile 2's page ids
+    // tiles 0 and 1 into the wave's two slots, with tile 2's page ids
     // between them as in the loop below. Issued after the query loads, so
     // that waiting for those never waits for the tiles.
     if (J > 0) {
       dma(slot_a, 0, P0);
       P2 = pages(min(2, J - 1));
-      dma(slot_b, 1, J > 1 ? P1 : P0);
+      if (J > 1) dma(slot_b, 1, P1);
     }
   }
 
@@ -751,28 +746,31 @@ void decode_split_kernel(const DecodeArgs a) {
     }
   } else if constexpr (LPIPE) {
     // Tile j sits in slot j % 2; once it is back in registers the slot takes
-    // tile j + 2 (past the last tile, a cache-hit copy that is never read:
-    // every iteration issues the same loads), so two tiles stream in while
-    // one is multiplied. The compiler does not order the buffer -> LDS
-    // copies before the reads of their slot, so each read is preceded by an
-    // explicit wait: issued after tile j's copies are exactly the next
-    // tile's copies (page ids are scalar loads), so waiting until that many
-    // vector-memory operations remain means tile j has landed.
+    // tile j + 2 (if there is one), so two tiles stream in while one is
+    // multiplied. The compiler does not order the buffer -> LDS copies before
+    // the reads of their slot, so each read is preceded by an explicit wait:
+    // issued after tile j's copies are exactly tile j + 1's copies if j + 1 <
+    // J and nothing otherwise (page ids are scalar loads), so waiting until
+    // that many vector-memory operations remain means tile j has landed.
     constexpr int kAfter = TILE_LOADS;
     constexpr int kWaitTile = (kAfter & 15) | ((kAfter >> 4) << 14) | 0x0F70;
     static_assert(kAfter < 64, "vmcnt holds 6 bits");
+    auto wait_tile = [&](int j) {
+      if (j + 1 < J) __builtin_amdgcn_s_waitcnt(kWaitTile);
+      else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    };
     if (J > 0) {
       for (int j = 0; j < J; j += 2) {
-        __builtin_amdgcn_s_waitcnt(kWaitTile);
+        wait_tile(j);
         unstage(A, slot_a);                         // (ends with its reads done)
         P0 = pages(min(j + 3, J - 1));
-        dma(slot_a, j + 2, P2);
+        if (j + 2 < J) dma(slot_a, j + 2, P2);
         compute(A, j);
         if (j + 1 >= J) break;
-        __builtin_amdgcn_s_waitcnt(kWaitTile);
+        wait_tile(j + 1);
         unstage(A, slot_b);
         P2 = pages(min(j + 4, J - 1));
-        dma(slot_b, j + 3, P0);
+        if (j + 3 < J) dma(slot_b, j + 3, P0);
         compute(A, j + 1);
       }
     }
