@@ -213,6 +213,10 @@ LDS_VERIFY_CASES = [
     ("e4m3", 3, (8, 70, 1500), 8, 64, 8, "f16"),
     ("e4m3", 2, (300, 2000), 12, 128, 0, "bf16"),
     ("e5m2", 1, (4100,), 16, 2048, 3, "bf16"),
+    # one partition: 5 and 10 tiles (waves with 1-3 tiles, so the last copy of a wave is
+    # waited for with none after it) and a 3-tile context (a wave with no tile)
+    ("e5m2", 3, (320, 593, 129), 16, 64, 1, "f16"),
+    ("e4m3", 2, (449, 200), 8, 128, 1, "bf16"),
 ]
 
 
