@@ -681,7 +681,7 @@ void decode_split_kernel(const DecodeArgs a) {
       // products, one product then four VALU instructions, in a scheduling
       // region of their own (the compiler otherwise issues the products in
       // runs, and the VALU work waits behind each run). With two blocks the
-      // same order measured 3-5% slower, so they keep the plain order.
+      // same order measured no faster, so they keep the plain order.
       softmax(0);
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
