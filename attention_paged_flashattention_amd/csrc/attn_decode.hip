@@ -185,7 +185,8 @@ __device__ __forceinline__ void lds_read_tile<8>(u32x4 (&r)[8], uint32_t addr) {
 // go to 8 dimension rows of the token's value group.
 template <int D, int FMT, int QT>
 __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, int b, int g, int p0,
-                                                  int i0, int i1, const int32_t* btb) {
+                                                  int i0, int i1, const int32_t* btb, int tid,
+                                                  int nthreads) {
   constexpr int ES = (FMT == KV_F16) ? 2 : 1;
   constexpr int CH = D / 8;                   // 16-byte source chunks per row
   const bool ksc = a.k_scale != nullptr, vsc = a.v_scale != nullptr;
@@ -196,7 +197,7 @@ __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, int b, in
   const int vg_log2 = bs_log2 < 6 ? bs_log2 : 6;
   const int64_t T = (int64_t)1 << vg_log2;
   const int tasks = (i1 - i0) * 2 * CH;
-  for (int e = threadIdx.x; e < tasks; e += 256) {
+  for (int e = tid; e < tasks; e += nthreads) {
     const int i = i0 + e / (2 * CH);
     const int r = e % (2 * CH);
     const bool isv = r >= CH;
@@ -480,14 +481,29 @@ void decode_split_kernel(const DecodeArgs a) {
 
   // Fused quantize-on-write: the work-group whose keys hold some of the new
   // tokens writes them for its KV head before any load (no other work-group
-  // reads those keys of this head). Each wave waits until its stores have
-  // reached the L2 (vmcnt 0: gfx9 counts stores there too), then the barrier
-  // orders them before every wave's loads of those keys.
+  // reads those keys of this head). With several new tokens every wave waits
+  // until its stores have reached the L2 (vmcnt 0: gfx9 counts stores there
+  // too, in issue order with the loads), then the barrier orders them before
+  // every wave's loads of those keys.
   if constexpr (APPEND) {
     const int p0 = ctx - a.q_len;   // position of new token 0
     const int i0 = max(0, tb - p0), i1 = min(a.q_len, te - p0);
-    if (i1 > i0) {
-      append_new_tokens<D, FMT, QT>(a, b, g, p0, i0, i1, btb);
+    if (i1 - i0 == 1) {
+      // One new token in this work-group's keys: only the wave whose tile
+      // holds it reads its slots (K row and value codes lie in that tile), so
+      // that wave writes it and no other wave waits. Its stores go out before
+      // its first tile's loads (the empty asm keeps the compiler from moving
+      // memory operations across), and the wave's memory operations complete
+      // in order: the wait for tile j - 2 covers the stores before tile j is
+      // loaded, and a token in the wave's first two tiles is waited for here.
+      const int t_idx = (p0 + i0 - tb) >> 6;   // the token's tile in the partition
+      if (w == (t_idx & 3)) {
+        append_new_tokens<D, FMT, QT>(a, b, g, p0, i0, i1, btb, lane, 64);
+        if ((t_idx >> 2) < 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
+      asm volatile("" ::: "memory");
+    } else if (i1 > i0) {
+      append_new_tokens<D, FMT, QT>(a, b, g, p0, i0, i1, btb, threadIdx.x, 256);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
     }
