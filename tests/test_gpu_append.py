@@ -76,6 +76,10 @@ CASES = [
     ("e4m3", "bf16", 3, (130, 63), 32, 64, 8, 2, 0),
     ("f16", "f16", 4, (100, 33), 32, 64, 8, 2, 0),
     ("f16", "f16", 1, (257, 1), 16, 128, 16, 2, 0),
+    # one partition: the new token's tile is a wave's second, third or later tile, in the
+    # register pipeline (FP8) and in the one-tile loop (fp16 cache); only that wave writes it
+    ("f16", "f16", 1, (700, 1100), 16, 128, 32, 8, 1),
+    ("e4m3", "f16", 1, (400, 600, 1030), 64, 128, 32, 8, 1),
     # more than 16 rows per KV head: the write kernel with block-table slots
     # runs before the plain kernel
     ("f16", "f16", 8, (100, 33), 32, 64, 8, 2, 0),
